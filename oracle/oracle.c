@@ -1,0 +1,226 @@
+/*
+ * CPU oracle for the context-sparse decode step.  TEST INFRASTRUCTURE ONLY:
+ * only the tests, the smoke check and the benchmark's CPU-baseline leg use it;
+ * the GPU library never links, loads or calls it, and it shares no code with
+ * the GPU library (it walks the page table and decodes bf16 on its own).
+ *
+ * What it computes, all in fp64, plainly and slowly:
+ *
+ *  scores   s[b,h,j] = sum_{d<128} q[b,h,d] * K[b, h/G, j, d]  for every cached
+ *           token j < N_b.  The raw query-key product: the numerator of scaled
+ *           dot-product attention, softmax(q K^T / sqrt(d_k)) V (sparse-attention
+ *           survey page, section 1.1).  Products of two bf16 values are exact in
+ *           fp64; d is summed in ascending order.  Query head h reads key/value
+ *           head floor(h / G), G = Hq / Hkv (contiguous GQA groups).
+ *
+ *  top-k    The exact "oracle top-k" indexer of the context-sparsity paper
+ *           (German summary, section 2, sparsity mechanisms: exact selection
+ *           of the top-k tokens): for each (b, h), k' = min(k_b, N_b) tokens,
+ *           ordered by score descending and, on equal scores, by lower token
+ *           index first.  Written out ascending by token index, padded with -1.
+ *
+ *  attend   Softmax attention over a given index set I (the sparse decode mode
+ *           of the paper's Fig. 1a reads only the selected rows): with the scale
+ *           c (1/sqrt(128) by default), l_j = c * s_j, m = max_I l_j,
+ *           w_j = exp(l_j - m), o = sum_I w_j V_j / sum_I w_j.  This is the
+ *           attention output o = V^T a with a a distribution over the tokens
+ *           (paper section 2.1, Theorem 1), restricted to I and renormalised.
+ *
+ *  dense    The same with I = {0, ..., N_b - 1} (the dense decode mode of
+ *           Fig. 1a, which reads the whole cache).
+ *
+ * Layouts: q [B][Hq][128] bf16 bits; caches [pages][Hkv][16][128] bf16 bits;
+ * page_table [B][max_pages] int32; seq_lens, k_per_seq [B] int32.
+ * Work is spread over (b, h) with OpenMP; nothing else is reordered.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORC_D 128
+#define ORC_PAGE 16
+
+typedef struct {
+    const uint16_t *k, *v;      /* bf16 bit patterns */
+    const int32_t *page_table;
+    const int32_t *seq_lens;
+    int32_t batch, num_kv_heads, max_pages;
+} orc_cache;
+
+static double bf16_value(uint16_t bits)
+{
+    uint32_t u = (uint32_t)bits << 16;  /* bf16 is the top half of an fp32 */
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* Address of token j's row for kv head g of sequence b. */
+static const uint16_t *row_of(const uint16_t *cache, const orc_cache *c, int b, int g, int64_t j)
+{
+    int64_t page = c->page_table[(int64_t)b * c->max_pages + j / ORC_PAGE];
+    int64_t slot = j % ORC_PAGE;
+    return cache + ((page * c->num_kv_heads + g) * ORC_PAGE + slot) * ORC_D;
+}
+
+static double dot_q_k(const uint16_t *qrow, const uint16_t *krow)
+{
+    double s = 0.0;
+    for (int d = 0; d < ORC_D; ++d)
+        s += bf16_value(qrow[d]) * bf16_value(krow[d]);
+    return s;
+}
+
+int oracle_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+void oracle_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
+/* scores_out: [B][Hq][n_stride] fp64; entries j >= N_b are left untouched. */
+void oracle_scores(const uint16_t *k_cache, const int32_t *page_table, const int32_t *seq_lens,
+                   int32_t batch, int32_t num_kv_heads, int32_t max_pages, const uint16_t *q,
+                   int32_t num_q_heads, int64_t n_stride, double *scores_out)
+{
+    orc_cache c = {k_cache, 0, page_table, seq_lens, batch, num_kv_heads, max_pages};
+    int32_t G = num_q_heads / num_kv_heads;
+    int64_t pairs = (int64_t)batch * num_q_heads;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t bh = 0; bh < pairs; ++bh) {
+        int b = (int)(bh / num_q_heads), h = (int)(bh % num_q_heads), g = h / G;
+        const uint16_t *qrow = q + bh * ORC_D;
+        double *out = scores_out + bh * n_stride;
+        for (int64_t j = 0; j < seq_lens[b]; ++j)
+            out[j] = dot_q_k(qrow, row_of(k_cache, &c, b, g, j));
+    }
+}
+
+/* Ordering used by the selection: higher score first, then lower index. */
+typedef struct { double s; int64_t j; } scored_token;
+
+static int by_score_then_index(const void *pa, const void *pb)
+{
+    const scored_token *a = (const scored_token *)pa, *b = (const scored_token *)pb;
+    if (a->s > b->s) return -1;
+    if (a->s < b->s) return 1;
+    return (a->j > b->j) - (a->j < b->j);
+}
+
+static int by_index(const void *pa, const void *pb)
+{
+    int32_t a = *(const int32_t *)pa, b = *(const int32_t *)pb;
+    return (a > b) - (a < b);
+}
+
+/*
+ * Exact top-k from precomputed scores [B][Hq][n_stride].
+ * idx_out [B][Hq][k_max]: the k' = min(k_b, N_b, k_max) selected token indices,
+ * ascending, then -1.  kth_out [B][Hq] (may be NULL): the k'-th largest score
+ * (the selection threshold s_(k')).
+ */
+void oracle_topk(const double *scores, const int32_t *seq_lens, const int32_t *k_per_seq,
+                 int32_t batch, int32_t num_q_heads, int64_t n_stride, int32_t k_max,
+                 int32_t *idx_out, double *kth_out)
+{
+    int64_t pairs = (int64_t)batch * num_q_heads;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t bh = 0; bh < pairs; ++bh) {
+        int b = (int)(bh / num_q_heads);
+        int64_t n = seq_lens[b];
+        int64_t kk = k_per_seq[b];
+        if (kk > n) kk = n;
+        if (kk > k_max) kk = k_max;
+        if (kk < 0) kk = 0;
+        scored_token *all = (scored_token *)malloc((size_t)(n > 0 ? n : 1) * sizeof *all);
+        for (int64_t j = 0; j < n; ++j) {
+            all[j].s = scores[bh * n_stride + j];
+            all[j].j = j;
+        }
+        qsort(all, (size_t)n, sizeof *all, by_score_then_index);
+        int32_t *row = idx_out + bh * k_max;
+        for (int64_t i = 0; i < kk; ++i)
+            row[i] = (int32_t)all[i].j;
+        qsort(row, (size_t)kk, sizeof *row, by_index);
+        for (int64_t i = kk; i < k_max; ++i)
+            row[i] = -1;
+        if (kth_out)
+            kth_out[bh] = kk > 0 ? all[kk - 1].s : -INFINITY;
+        free(all);
+    }
+}
+
+/* Softmax attention of one (b, h) over the listed tokens; n_sel entries of sel
+ * (entries < 0 are skipped).  out: 128 fp64.  With no tokens the output is 0. */
+static void attend_one(const orc_cache *c, int b, int g, const uint16_t *qrow, const int32_t *sel,
+                       int64_t n_sel, double scale, double *out)
+{
+    double m = -INFINITY;
+    for (int64_t i = 0; i < n_sel; ++i) {
+        if (sel[i] < 0) continue;
+        double l = scale * dot_q_k(qrow, row_of(c->k, c, b, g, sel[i]));
+        if (l > m) m = l;
+    }
+    double z = 0.0, acc[ORC_D];
+    for (int d = 0; d < ORC_D; ++d) acc[d] = 0.0;
+    for (int64_t i = 0; i < n_sel; ++i) {
+        if (sel[i] < 0) continue;
+        double w = exp(scale * dot_q_k(qrow, row_of(c->k, c, b, g, sel[i])) - m);
+        const uint16_t *vrow = row_of(c->v, c, b, g, sel[i]);
+        z += w;
+        for (int d = 0; d < ORC_D; ++d)
+            acc[d] += w * bf16_value(vrow[d]);
+    }
+    for (int d = 0; d < ORC_D; ++d)
+        out[d] = z > 0.0 ? acc[d] / z : 0.0;
+}
+
+/* Sparse attention over idx [B][Hq][k_max] (-1 = unused); out [B][Hq][128] fp64. */
+void oracle_attend(const uint16_t *k_cache, const uint16_t *v_cache, const int32_t *page_table,
+                   const int32_t *seq_lens, int32_t batch, int32_t num_kv_heads, int32_t max_pages,
+                   const uint16_t *q, int32_t num_q_heads, const int32_t *idx, int32_t k_max,
+                   double scale, double *out)
+{
+    orc_cache c = {k_cache, v_cache, page_table, seq_lens, batch, num_kv_heads, max_pages};
+    int32_t G = num_q_heads / num_kv_heads;
+    int64_t pairs = (int64_t)batch * num_q_heads;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t bh = 0; bh < pairs; ++bh) {
+        int b = (int)(bh / num_q_heads), h = (int)(bh % num_q_heads);
+        attend_one(&c, b, h / G, q + bh * ORC_D, idx + bh * k_max, k_max, scale, out + bh * ORC_D);
+    }
+}
+
+/* Dense attention over every cached token; out [B][Hq][128] fp64. */
+void oracle_dense(const uint16_t *k_cache, const uint16_t *v_cache, const int32_t *page_table,
+                  const int32_t *seq_lens, int32_t batch, int32_t num_kv_heads, int32_t max_pages,
+                  const uint16_t *q, int32_t num_q_heads, double scale, double *out)
+{
+    orc_cache c = {k_cache, v_cache, page_table, seq_lens, batch, num_kv_heads, max_pages};
+    int32_t G = num_q_heads / num_kv_heads;
+    int64_t pairs = (int64_t)batch * num_q_heads;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t bh = 0; bh < pairs; ++bh) {
+        int b = (int)(bh / num_q_heads), h = (int)(bh % num_q_heads);
+        int64_t n = seq_lens[b];
+        int32_t *all = (int32_t *)malloc((size_t)(n > 0 ? n : 1) * sizeof *all);
+        for (int64_t j = 0; j < n; ++j) all[j] = (int32_t)j;
+        attend_one(&c, b, h / G, q + bh * ORC_D, all, n, scale, out + bh * ORC_D);
+        free(all);
+    }
+}

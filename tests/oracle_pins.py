@@ -1,0 +1,306 @@
+"""Pins for the fp64 oracle: checks against what the definitions and mathematics fix.
+
+Each pin takes the oracle's ctypes library handle, so the same checks can run
+against builds of oracle.c with planted mistakes (tests/test_oracle_mutants.py).
+None of them recomputes a result the way the oracle does:
+
+* top-k:   brute force over every subset on tiny inputs (the unique set whose
+           every member beats every non-member under score desc, index asc) and
+           an independent rank count;
+* scores:  exact rational arithmetic on logical (unpaged) tensors; integer
+           inputs; shift invariance;
+* attend:  the softmax formula without max-subtraction in 40-digit decimal
+           arithmetic; uniform values; uniform keys; a one-hot key closed form;
+           k = 1 returning the argmax row exactly;
+* dense:   equal to attending over every index (k = N) and to the closed forms;
+* layout:  identical results under contiguous, shuffled and fragmented pages.
+"""
+from __future__ import annotations
+
+import itertools
+import math
+from decimal import Decimal, getcontext
+from fractions import Fraction
+
+import numpy as np
+
+import oracle
+from helpers import TinyCase, bf16_round, random_case
+
+SCALE = oracle.DEFAULT_SCALE
+
+
+def _cache(case: TinyCase) -> oracle.Cache:
+    return oracle.Cache(case.k_cache, case.v_cache, case.page_table, case.lens, case.num_kv_heads)
+
+
+def _exact_scores(case: TinyCase):
+    """Exact rational q.K per (b, h, j) from the logical tensors."""
+    out = []
+    G = case.group
+    for b in range(case.batch):
+        per_h = []
+        for h in range(case.num_q_heads):
+            qf = [Fraction(float(x)) for x in case.q_f[b, h]]
+            rows = case.k_f[b][h // G]
+            per_h.append([sum(qf[d] * Fraction(float(rows[j, d])) for d in range(128))
+                          for j in range(rows.shape[0])])
+        out.append(per_h)
+    return out
+
+
+def _brute_force_topk(s, k):
+    """The unique size-k subset whose every member beats every non-member."""
+    n = len(s)
+    beats = lambda i, j: s[i] > s[j] or (s[i] == s[j] and i < j)
+    found = [set(c) for c in itertools.combinations(range(n), k)
+             if all(beats(i, j) for i in c for j in range(n) if j not in c)]
+    assert len(found) == 1
+    return sorted(found[0])
+
+
+# ---------------------------------------------------------------------------- top-k
+
+def pin_topk_bruteforce(lib):
+    rng = np.random.default_rng(11)
+    for trial in range(60):
+        B, hq = 2, 3
+        n = int(rng.integers(1, 10))
+        lens = np.array([n, max(1, n - int(rng.integers(0, 3)))], dtype=np.int32)
+        if trial % 2:
+            s = rng.integers(-2, 3, size=(B, hq, n)).astype(np.float64)     # many ties
+        else:
+            s = rng.standard_normal((B, hq, n))
+        kvec = rng.integers(0, n + 3, size=B).astype(np.int32)
+        k_max = int(max(1, kvec.max()))
+        if trial % 3 == 2:                       # a row narrower than k: keep the best k_max
+            k_max = int(rng.integers(1, k_max + 1))
+        idx, kth = oracle.topk(s, lens, kvec, k_max, lib=lib)
+        for b in range(B):
+            kp = int(min(kvec[b], lens[b], k_max))
+            for h in range(hq):
+                sl = list(s[b, h, :lens[b]])
+                want = _brute_force_topk(sl, kp) if kp > 0 else []
+                got = list(idx[b, h])
+                assert got[:kp] == want, (trial, b, h, got, want)
+                assert all(x == -1 for x in got[kp:])
+                if kp > 0:
+                    assert kth[b, h] == sorted(sl, reverse=True)[kp - 1]
+
+
+def pin_topk_rank_count(lib):
+    rng = np.random.default_rng(12)
+    n = 300
+    s = rng.integers(-4, 5, size=(1, 4, n)).astype(np.float64)
+    s[0, 1] = rng.standard_normal(n)
+    s[0, 2] = 0.0                                                      # all tied
+    for k in (1, 7, 150, 299, 300, 301):
+        idx, _ = oracle.topk(s, np.array([n], np.int32), np.array([k], np.int32), max(k, 1), lib=lib)
+        kp = min(k, n)
+        for h in range(4):
+            sh = s[0, h]
+            rank = np.array([np.sum((sh > sh[j]) | ((sh == sh[j]) & (np.arange(n) < j))) for j in range(n)])
+            want = np.nonzero(rank < kp)[0]
+            assert np.array_equal(idx[0, h, :kp], want), (k, h)
+
+
+# ---------------------------------------------------------------------------- scores
+
+def pin_scores_exact(lib):
+    rng = np.random.default_rng(13)
+    case = random_case(rng, batch=2, hq=6, hkv=2, lens=[5, 37], layout="shuffled")
+    got = oracle.scores(_cache(case), case.q, lib=lib)
+    ex = _exact_scores(case)
+    for b in range(case.batch):
+        for h in range(case.num_q_heads):
+            for j in range(case.lens[b]):
+                e = float(ex[b][h][j])
+                assert abs(got[b, h, j] - e) <= 1e-12 * max(1.0, abs(e)), (b, h, j, got[b, h, j], e)
+
+
+def pin_scores_integer(lib):
+    rng = np.random.default_rng(14)
+    case = random_case(rng, batch=2, hq=8, hkv=2, lens=[40, 19], layout="fragmented", integer=True)
+    got = oracle.scores(_cache(case), case.q, lib=lib)
+    G = case.group
+    for b in range(case.batch):
+        for h in range(case.num_q_heads):
+            qi = case.q_f[b, h].astype(np.int64)
+            ki = case.k_f[b][h // G].astype(np.int64)
+            want = ki @ qi
+            assert np.array_equal(got[b, h, :case.lens[b]], want.astype(np.float64)), (b, h)
+
+
+def pin_shift_invariance(lib):
+    """Adding an integer vector u to every key shifts every score of a head by q.u:
+    the selection (strict) and the softmax output are unchanged."""
+    rng = np.random.default_rng(15)
+    base = random_case(rng, batch=1, hq=4, hkv=1, lens=[48], integer=True)
+    u = rng.integers(-3, 4, size=128).astype(np.float64)
+    shifted = TinyCase([k + u[None, None, :] for k in base.k_f], base.v_f, base.q_f, seed=8)
+    kvec = np.array([9], np.int32)
+    s0 = oracle.scores(_cache(base), base.q, lib=lib)
+    s1 = oracle.scores(_cache(shifted), shifted.q, lib=lib)
+    for h in range(4):
+        assert np.array_equal(s1[0, h] - s0[0, h], np.full(48, float(base.q_f[0, h] @ u)))
+    i0, _ = oracle.topk(s0, base.lens, kvec, 9, lib=lib)
+    i1, _ = oracle.topk(s1, shifted.lens, kvec, 9, lib=lib)
+    assert np.array_equal(i0, i1)
+    o0 = oracle.attend(_cache(base), base.q, i0, SCALE, lib=lib)
+    o1 = oracle.attend(_cache(shifted), shifted.q, i1, SCALE, lib=lib)
+    assert np.allclose(o0, o1, rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------- attend
+
+def pin_attend_decimal(lib):
+    """Softmax without max-subtraction, in 40-digit decimal arithmetic."""
+    getcontext().prec = 40
+    rng = np.random.default_rng(16)
+    case = random_case(rng, batch=2, hq=4, hkv=2, lens=[21, 34], layout="shuffled")
+    k_max = 12
+    idx = np.full((2, 4, k_max), -1, dtype=np.int32)
+    for b in range(2):
+        for h in range(4):
+            m = int(rng.integers(1, k_max + 1))
+            sel = np.sort(rng.choice(case.lens[b], size=m, replace=False))
+            slots = np.sort(rng.choice(k_max, size=m, replace=False))   # -1 holes anywhere
+            idx[b, h, slots] = sel
+    got = oracle.attend(_cache(case), case.q, idx, SCALE, lib=lib)
+    ex = _exact_scores(case)
+    sc = Decimal(SCALE)
+    for b in range(2):
+        for h in range(4):
+            sel = [int(j) for j in idx[b, h] if j >= 0]
+            w = [(sc * Decimal(ex[b][h][j].numerator) / Decimal(ex[b][h][j].denominator)).exp() for j in sel]
+            z = sum(w)
+            g = h // case.group
+            for d in range(128):
+                num = sum(wi * Decimal(float(case.v_f[b][g][j, d])) for wi, j in zip(w, sel))
+                want = float(num / z)
+                assert abs(got[b, h, d] - want) <= 1e-12 * max(1.0, abs(want)), (b, h, d)
+
+
+def pin_uniform_values(lib):
+    rng = np.random.default_rng(17)
+    case = random_case(rng, batch=2, hq=4, hkv=2, lens=[33, 16])
+    v = [np.broadcast_to(bf16_round(rng.standard_normal((2, 1, 128))), (2, n, 128)).copy() for n in case.lens]
+    uni = TinyCase(case.k_f, v, case.q_f)
+    idx = np.full((2, 4, 8), -1, np.int32)
+    idx[:, :, :5] = [0, 3, 4, 9, 15]
+    for out in (oracle.attend(_cache(uni), uni.q, idx, SCALE, lib=lib), oracle.dense(_cache(uni), uni.q, SCALE, lib=lib)):
+        for b in range(2):
+            for h in range(4):
+                assert np.allclose(out[b, h], v[b][h // 2][0], rtol=1e-14, atol=1e-14)
+
+
+def pin_uniform_keys(lib):
+    """Identical keys: every score ties, the first k' indices win, o = mean of their values."""
+    rng = np.random.default_rng(18)
+    n = 41
+    krow = bf16_round(rng.standard_normal(128))
+    k = [np.broadcast_to(krow, (1, n, 128)).copy()]
+    v = [bf16_round(rng.standard_normal((1, n, 128)))]
+    case = TinyCase(k, v, bf16_round(rng.standard_normal((1, 3, 128))))
+    for kk in (1, 5, 40, 41, 60):
+        s = oracle.scores(_cache(case), case.q, lib=lib)
+        idx, _ = oracle.topk(s, case.lens, np.array([kk], np.int32), kk, lib=lib)
+        kp = min(kk, n)
+        for h in range(3):
+            assert np.array_equal(idx[0, h, :kp], np.arange(kp))
+        out = oracle.attend(_cache(case), case.q, idx, SCALE, lib=lib)
+        want = v[0][0, :kp].mean(axis=0)
+        assert np.allclose(out[0], want[None, :], rtol=1e-13, atol=1e-14)
+    dense = oracle.dense(_cache(case), case.q, SCALE, lib=lib)
+    assert np.allclose(dense[0], v[0][0].mean(axis=0)[None, :], rtol=1e-13, atol=1e-14)
+
+
+def pin_one_hot(lib):
+    """K_{j*} = c e_m, all other keys 0: S = {j*} + the first k'-1 other indices, and
+    o = a V_{j*} + (1-a)/(k'-1) sum_{S minus j*} V with a = e^x / (e^x + k' - 1), x = c q_m / sqrt(128)."""
+    rng = np.random.default_rng(19)
+    n, m, jstar, c = 50, 17, 37, 4.0
+    for sign in (1.0, -1.0):
+        q = bf16_round(rng.standard_normal((1, 2, 128)))
+        q[0, :, m] = sign * np.array([1.5, 0.75])
+        k = np.zeros((1, 1, n, 128))
+        k[0, 0, jstar, m] = c
+        v = bf16_round(rng.standard_normal((1, 1, n, 128)))
+        case = TinyCase([k[0]], [v[0]], q)
+        for kk in (1, 6, 20):
+            s = oracle.scores(_cache(case), case.q, lib=lib)
+            idx, _ = oracle.topk(s, case.lens, np.array([kk], np.int32), kk, lib=lib)
+            out = oracle.attend(_cache(case), case.q, idx, SCALE, lib=lib)
+            for h in range(2):
+                if sign > 0:
+                    others = [j for j in range(n) if j != jstar][:kk - 1]
+                    want_set = sorted([jstar] + others)
+                    x = c * q[0, h, m] * SCALE
+                    a = math.exp(x) / (math.exp(x) + kk - 1)
+                    want_o = a * v[0, 0, jstar] + ((1 - a) / (kk - 1) * v[0, 0, others].sum(axis=0) if kk > 1 else 0)
+                else:
+                    want_set = list(range(kk))
+                    want_o = v[0, 0, :kk].mean(axis=0)
+                assert list(idx[0, h]) == want_set, (sign, kk, h)
+                assert np.allclose(out[0, h], want_o, rtol=1e-12, atol=1e-13), (sign, kk, h)
+
+
+def pin_k1_argmax_row(lib):
+    rng = np.random.default_rng(20)
+    case = random_case(rng, batch=2, hq=4, hkv=1, lens=[29, 64])
+    s = oracle.scores(_cache(case), case.q, lib=lib)
+    idx, _ = oracle.topk(s, case.lens, np.array([1, 1], np.int32), 1, lib=lib)
+    out = oracle.attend(_cache(case), case.q, idx, SCALE, lib=lib)
+    ex = _exact_scores(case)
+    for b in range(2):
+        for h in range(4):
+            j = int(np.argmax([float(x) for x in ex[b][h]]))
+            assert idx[0 + b, h, 0] == j
+            assert np.array_equal(out[b, h], case.v_f[b][0][j])
+
+
+# ---------------------------------------------------------------------------- dense / invariants
+
+def pin_dense_is_attend_all(lib):
+    rng = np.random.default_rng(21)
+    case = random_case(rng, batch=3, hq=10, hkv=2, lens=[1, 17, 45], layout="fragmented")
+    n_max = int(case.lens.max())
+    idx = np.full((3, 10, n_max), -1, np.int32)
+    for b in range(3):
+        idx[b, :, :case.lens[b]] = np.arange(case.lens[b])
+    d = oracle.dense(_cache(case), case.q, SCALE, lib=lib)
+    a = oracle.attend(_cache(case), case.q, idx, SCALE, lib=lib)
+    assert np.allclose(d, a, rtol=1e-12, atol=1e-14)
+    s = oracle.scores(_cache(case), case.q, lib=lib)
+    i2, _ = oracle.topk(np.nan_to_num(s, nan=-1e300), case.lens, case.lens, n_max, lib=lib)
+    assert np.array_equal(i2, idx)                           # k >= N selects everything
+    # a direct fp64 softmax on the logical tensors (max-subtracted, numpy)
+    for b in range(3):
+        for h in range(10):
+            sc = case.k_f[b][h // 5] @ case.q_f[b, h] * SCALE
+            w = np.exp(sc - sc.max())
+            want = (w[:, None] * case.v_f[b][h // 5]).sum(0) / w.sum()
+            assert np.allclose(d[b, h], want, rtol=1e-11, atol=1e-13)
+
+
+def pin_layout_invariance(lib):
+    rng = np.random.default_rng(22)
+    base = random_case(rng, batch=3, hq=4, hkv=2, lens=[37, 16, 70], layout="contiguous")
+    res = []
+    for layout, seed in (("contiguous", 1), ("shuffled", 2), ("fragmented", 3)):
+        case = TinyCase(base.k_f, base.v_f, base.q_f, layout=layout, seed=seed)
+        s = oracle.scores(_cache(case), case.q, lib=lib)
+        idx, kth = oracle.topk(np.nan_to_num(s, nan=0.0), case.lens, np.array([5, 16, 9], np.int32), 16, lib=lib)
+        out = oracle.attend(_cache(case), case.q, idx, SCALE, lib=lib)
+        dn = oracle.dense(_cache(case), case.q, SCALE, lib=lib)
+        res.append((np.nan_to_num(s), idx, kth, out, dn))
+    for other in res[1:]:
+        for x, y in zip(res[0], other):
+            assert np.array_equal(x, y)
+
+
+ALL_PINS = [
+    pin_topk_bruteforce, pin_topk_rank_count, pin_scores_exact, pin_scores_integer,
+    pin_shift_invariance, pin_attend_decimal, pin_uniform_values, pin_uniform_keys, pin_one_hot,
+    pin_k1_argmax_row, pin_dense_is_attend_all, pin_layout_invariance,
+]
