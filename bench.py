@@ -1,0 +1,259 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark of the context-sparse decode path on one MI355X.
+
+A step is one attention layer of sparse decode for the whole batch: the exact
+top-k indexer (score pass + radix select) followed by the gather-attend over the
+selected rows (plus the one-token cache append on workloads that grow).  The
+dense decode of the same layer is timed the same way for comparison.  Inputs are
+seeded synthetic bf16 caches already resident in HBM when timing starts.
+
+Prints ONE JSON line: steps/s (value), the per-kernel roofline of the dominant
+launch group (the indexer) against the 8 TB/s HBM peak, and the fp64 CPU oracle
+timed on the host as a reported baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode steps/s + effective HBM GB/s (% of peak) at 50x sparsity vs dense"
+PEAK_HBM_BPS = 8.0e12          # MI355X HBM3E peak
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_index_topk_C2.txt")
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=2, help="decode configuration 1-5 (default 2)")
+    ap.add_argument("--ratio", type=int, default=50, help="sparsity N/k (default 50)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--cold", action="store_true", help="also time each launch group after a 1 GiB cache flush")
+    return ap.parse_args()
+
+
+def algorithmic_bytes(seq_lens, kps, B, hq, hkv):
+    """Bytes each piece must move at minimum (bf16 rows of 256 B)."""
+    n = np.asarray(seq_lens, np.int64)
+    k = np.asarray(kps, np.int64)
+    q_bytes = B * hq * 128 * 2
+    out_bytes = B * hq * 128 * 4
+    index = int((hkv * n * 256).sum() + q_bytes + (hq * k * 4).sum())
+    attend = int((hq * k * (512 + 4)).sum() + q_bytes + out_bytes)
+    dense = int((hkv * n * 512).sum() + q_bytes + out_bytes)
+    return index, attend, dense
+
+
+def read_traffic():
+    """HBM bytes per launch of the indexer from the committed counter summary, if any."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    vals = {}
+    for line in open(TRAFFIC_FILE):
+        if ":" in line and not line.lstrip().startswith("#"):
+            key, val = line.split(":", 1)
+            vals[key.strip()] = val.strip()
+    try:
+        return float(vals["hbm_bytes_per_launch"]) if vals.get("kernel_source_sha") == source_sha() else None
+    except (KeyError, ValueError):
+        return None
+
+
+def source_sha():
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("index_topk.hip", "sdi_device.hpp"):
+        h.update(open(os.path.join(ROOT, "sparse_attention_decode_index_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def cpu_baseline(wl, target_s):
+    """The fp64 oracle (untuned) on the host: whole decode steps of the same workload."""
+    import oracle
+    cache = oracle.Cache.of(wl)
+    kps, k_max = wl.k_per_seq(), wl.k_max()
+    t0 = time.perf_counter()
+    steps = 0
+    while True:
+        oracle.decode_step(cache, wl.q, kps, k_max)
+        steps += 1
+        el = time.perf_counter() - t0
+        if el >= target_s or el / steps * (steps + 1) > 2.5 * target_s:
+            break
+    return {"value": steps / el, "unit": "decode steps/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{steps} whole decode step(s) of the same workload (scores, exact top-k, attend; fp64) "
+                      f"in {el:.1f} s"}
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: the sparse decode path here has no multi-GPU mode "
+              f"(asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import synth
+    import sparse_attention_decode_index_amd as sdi
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t_setup = time.perf_counter()
+    wl = synth.config(args.config, ratio=args.ratio)
+    B, hq, hkv = wl.batch, wl.num_q_heads, wl.num_kv_heads
+
+    def bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    k_cache, v_cache = bf16(wl.k_cache), bf16(wl.v_cache)
+    page_table = torch.from_numpy(wl.page_table).to(dev)
+    seq_lens = torch.from_numpy(wl.seq_lens).to(dev)
+    total = args.warmup + args.steps
+    growth = wl.steps > 1
+    # a fresh query per step; growing workloads also append one token per step (and recompute k)
+    n_q = min(total, 64) if not growth else min(total, wl.steps)
+    qs = [bf16(synth.queries(wl.seed, s, B, hq)) for s in range(n_q)]
+    appends, kps_steps, nmax_steps = [], [], []
+    host = wl
+    for s in range(n_q if growth else 1):
+        kps_steps.append(torch.from_numpy(host.k_per_seq()).to(dev))
+        nmax_steps.append(host.n_max)
+        if growth and s + 1 < n_q:
+            tok, pages, slots, kr, vr = host.new_rows()
+            appends.append((torch.from_numpy(pages).to(dev), torch.from_numpy(slots).to(dev), bf16(kr), bf16(vr)))
+            host.seq_lens = (host.seq_lens + 1).astype(np.int32)
+    seq_lens_steps = None
+    if growth:           # restore: the device cache starts at step 0
+        host.seq_lens = (host.seq_lens - (n_q - 1)).astype(np.int32)
+        seq_lens_steps = [torch.from_numpy((host.seq_lens + s).astype(np.int32)).to(dev) for s in range(n_q)]
+    k_max = int(max(int(t.max().item()) for t in kps_steps))
+    n_max_all = max(nmax_steps)
+    kv_full = sdi.PagedKV(k_cache, v_cache, page_table, seq_lens, n_max=n_max_all)
+    idx = torch.empty((B, hq, k_max), dtype=torch.int32, device=dev)
+    out = torch.empty((B, hq, 128), dtype=torch.float32, device=dev)
+    ws_index = torch.empty(max(1, sdi.index_topk_workspace_bytes(kv_full, hq, k_max)), dtype=torch.uint8, device=dev)
+    ws_attend = torch.empty(max(1, sdi.attend_workspace_bytes(kv_full, hq, k_max)), dtype=torch.uint8, device=dev)
+    ws_dense = torch.empty(max(1, sdi.dense_workspace_bytes(kv_full, hq)), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    setup_s = time.perf_counter() - t_setup
+    stream = torch.cuda.current_stream()
+
+    def step_args(s):
+        j = s % n_q
+        sl = seq_lens_steps[j] if growth else seq_lens
+        kv = sdi.PagedKV(k_cache, v_cache, page_table, sl, n_max=nmax_steps[j] if growth else wl.n_max)
+        return kv, qs[j], kps_steps[j if growth else 0]
+
+    def run_step(s, ev=None):
+        j = s % n_q
+        if growth and j > 0:                              # a0: append this step's token (plain copies)
+            pg, sl_, kr, vr = appends[j - 1]
+            k_cache[pg, :, sl_, :] = kr
+            v_cache[pg, :, sl_, :] = vr
+        kv, q, kps = step_args(s)
+        if ev is not None:
+            ev[0].record(stream)
+        sdi.index_topk(kv, q, kps, k_max, idx_out=idx, workspace=ws_index, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        sdi.attend(kv, q, idx, kps, out=out, workspace=ws_attend, stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for s in range(args.warmup):
+        run_step(s)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        run_step(args.warmup + s, evs[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    t_index = np.array([e[0].elapsed_time(e[1]) for e in evs]) * 1e-3
+    t_attend = np.array([e[1].elapsed_time(e[2]) for e in evs]) * 1e-3
+    t_step_gpu = evs[0][0].elapsed_time(evs[-1][2]) * 1e-3 / args.steps if args.steps > 1 else wall
+    ms_per_step = wall / args.steps * 1e3
+
+    # dense decode of the same layer
+    dense_s = None
+    if not args.no_dense:
+        for s in range(min(args.warmup, 5)):
+            kv, q, _ = step_args(s)
+            sdi.dense(kv, q, out=out, workspace=ws_dense, stream=stream)
+        torch.cuda.synchronize()
+        dsteps = max(10, args.steps // 2)
+        dev_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(dsteps)]
+        for s in range(dsteps):
+            kv, q, _ = step_args(s)
+            dev_ev[s][0].record(stream)
+            sdi.dense(kv, q, out=out, workspace=ws_dense, stream=stream)
+            dev_ev[s][1].record(stream)
+        torch.cuda.synchronize()
+        dense_s = float(np.mean([e[0].elapsed_time(e[1]) for e in dev_ev]) * 1e-3)
+
+    cold = {}
+    if args.cold:
+        flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        ci, ca = [], []
+        for s in range(10):
+            flush.fill_(s & 0xFF)
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            run_step(s, e)
+            torch.cuda.synchronize()
+            ci.append(e[0].elapsed_time(e[1]) * 1e-3)
+            ca.append(e[1].elapsed_time(e[2]) * 1e-3)
+        cold = {"index_us_cold": float(np.median(ci) * 1e6), "attend_us_cold": float(np.median(ca) * 1e6)}
+        del flush
+
+    kps0 = wl.k_per_seq()
+    b_index, b_attend, b_dense = algorithmic_bytes(wl.seq_lens, kps0, B, hq, hkv)
+    mi, ma = float(t_index.mean()), float(t_attend.mean())
+    step_bytes = b_index + b_attend
+    value = args.steps / wall
+    traffic = read_traffic()
+    roofline = {"bound": "hbm", "kernel": "index_topk (zero_u32_kernel + score_kernel + select_kernel)",
+                "achieved": b_index / mi / 1e9, "peak": PEAK_HBM_BPS / 1e9, "unit": "GB/s",
+                "frac": b_index / mi / PEAK_HBM_BPS, "traffic": traffic,
+                "algorithmic_bytes_per_launch": b_index, "avg_launch_us": mi * 1e6}
+    roofline_attend = {"bound": "hbm", "kernel": "attend (attend_kernel + merge_kernel)",
+                       "achieved": b_attend / ma / 1e9, "peak": PEAK_HBM_BPS / 1e9, "unit": "GB/s",
+                       "frac": b_attend / ma / PEAK_HBM_BPS, "algorithmic_bytes_per_launch": b_attend,
+                       "avg_launch_us": ma * 1e6}
+    result = {
+        "metric": METRIC, "value": value, "unit": "decode steps/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": synth.CONFIG_NAMES[args.config] + (f" (ratio {args.ratio})" if args.ratio != 50 else ""),
+                   "batch": B, "num_q_heads": hq, "num_kv_heads": hkv, "head_dim": 128, "page_size": 16,
+                   "context_max": int(wl.n_max), "k_max": k_max, "sparsity": args.ratio,
+                   "layout": wl.meta.get("layout"), "parallelism": "single GPU"},
+        "step_GBps": step_bytes / (mi + ma) / 1e9, "step_pct_of_peak": 100 * step_bytes / (mi + ma) / PEAK_HBM_BPS,
+        "index_us": mi * 1e6, "attend_us": ma * 1e6, "gpu_step_us": t_step_gpu * 1e6,
+        "roofline": roofline, "roofline_attend": roofline_attend,
+    }
+    if dense_s is not None:
+        result.update({"dense_us": dense_s * 1e6, "dense_steps_per_s": 1.0 / dense_s,
+                       "dense_GBps": b_dense / dense_s / 1e9, "dense_pct_of_peak": 100 * b_dense / dense_s / PEAK_HBM_BPS,
+                       "speedup_vs_dense": dense_s / (wall / args.steps),
+                       "attend_speedup_vs_dense": dense_s / ma})
+    result.update(cold)
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(wl if not growth else synth.config(args.config, ratio=args.ratio),
+                                              args.cpu_seconds)
+    result["setup_s"] = setup_s
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

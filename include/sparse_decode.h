@@ -1,0 +1,140 @@
+/*
+ * sparse_decode.h -- C ABI of the context-sparse decode library (gfx950 / MI355X).
+ *
+ * What it computes.  One decode step of attention over a paged bf16 KV cache,
+ * for every query head of every sequence in a batch:
+ *
+ *   index   the exact top-k indexer: score every cached key with the raw product
+ *           q.K^T and keep the k highest tokens (lower token index first on equal
+ *           scores).  This is the "oracle top-k" selection of the context-sparsity
+ *           paper (arXiv 2605.24168; German technical summary, section 2,
+ *           sparsity mechanisms) and the "lightweight indexer" of its Fig. 1a.
+ *   attend  softmax attention over only the selected rows, the sparse decode mode
+ *           of Fig. 1a (O(k d) bytes per step instead of O(N d)), with selections
+ *           that differ per token, per query and per head under GQA (paper
+ *           section 1, "sparsity can serve system gains").
+ *   dense   the dense decode mode of Fig. 1a: softmax attention over every cached
+ *           token, the reference the sparse mode is measured against.
+ * The attention form is scaled dot-product attention, softmax(q K^T / sqrt(d)) V
+ * (sparse-attention survey page, section 1.1); the output is o = V^T a with a a
+ * distribution over the attended tokens (paper section 2.1, Theorem 1).
+ *
+ * Memory.  Every pointer argument is a DEVICE pointer owned by the caller, except
+ * the sdi_kv struct itself, which is a HOST struct read during the call and never
+ * retained.  The library allocates nothing: each call takes a caller-provided
+ * device workspace whose size the matching *_workspace() function returns.
+ *
+ * Streams.  `stream` is a hipStream_t (NULL = the null stream).  Calls only
+ * enqueue kernels; results are valid once the stream has reached them.  The
+ * library holds no global state, so calls on different streams with different
+ * workspaces may overlap; two in-flight calls must not share a workspace.
+ *
+ * Errors.  Every check runs on the host before anything is enqueued; a call that
+ * returns an error has enqueued nothing.  SDI_ERR_HIP reports a failed launch.
+ * Device-side contents are the caller's contract and are not validated:
+ * 1 <= seq_lens[b] <= n_max, page-table entries of the first ceil(seq_lens[b]/16)
+ * pages in [0, num_pages), finite cache and query values.
+ */
+#ifndef SPARSE_DECODE_H
+#define SPARSE_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define SDI_API __attribute__((visibility("default")))
+#else
+#define SDI_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    SDI_OK = 0,
+    SDI_ERR_NULL = -1,       /* a required pointer is NULL */
+    SDI_ERR_SHAPE = -2,      /* head_dim != 128, page_size != 16, heads not a multiple, sizes < 1 ... */
+    SDI_ERR_K = -3,          /* k_max < 1 */
+    SDI_ERR_WORKSPACE = -4,  /* workspace smaller than the *_workspace() size */
+    SDI_ERR_HIP = -5         /* a kernel launch failed */
+};
+
+/*
+ * The paged KV cache (host struct describing device memory).
+ *   k_cache, v_cache  bf16 [num_pages][num_kv_heads][page_size][head_dim]: each
+ *                     (page, kv head) block is 16 rows x 256 B = 4 KiB contiguous.
+ *   page_table        int32 [batch][max_pages_per_seq]: token j of sequence b is
+ *                     row j % 16 of page page_table[b][j / 16].
+ *   seq_lens          int32 [batch]: cached tokens N_b of each sequence.
+ *   n_max             host copy of max_b N_b (sizes launches and workspaces).
+ * head_dim must be 128 and page_size 16.  A contiguous cache is the same layout
+ * with an identity page table.
+ */
+typedef struct sdi_kv {
+    const void *k_cache;
+    const void *v_cache;
+    const int32_t *page_table;
+    const int32_t *seq_lens;
+    int32_t batch;
+    int32_t num_kv_heads;
+    int32_t head_dim;
+    int32_t page_size;
+    int32_t max_pages_per_seq;
+    int32_t num_pages;
+    int32_t n_max;
+} sdi_kv;
+
+/*
+ * Exact top-k indexer (paper Fig. 1a "lightweight indexer"; German summary
+ * section 2, exact oracle top-k; per query head, section 1).
+ *   q          bf16 [batch][num_q_heads][128]; query head h reads kv head
+ *              h / (num_q_heads / num_kv_heads) (contiguous GQA groups).
+ *   k_per_seq  int32 [batch]: k_b.  Each (b, h) selects k' = min(k_b, N_b, k_max)
+ *              tokens: the k' largest scores s_j = q . K_j (fp32 accumulation of
+ *              bf16 products), ties going to the lower index.
+ *   idx_out    int32 [batch][num_q_heads][k_max]: the k' indices ascending, then -1.
+ *   ws         device workspace of at least sparse_decode_index_topk_workspace() bytes.
+ * Reads k_cache only (v_cache may be NULL).
+ */
+SDI_API int sparse_decode_index_topk(const sdi_kv *kv, const void *q, int32_t num_q_heads,
+                             const int32_t *k_per_seq, int32_t k_max, int32_t *idx_out,
+                             void *ws, size_t ws_bytes, void *stream);
+
+SDI_API size_t sparse_decode_index_topk_workspace(const sdi_kv *kv, int32_t num_q_heads, int32_t k_max);
+
+/*
+ * Sparse gather-attend (paper Fig. 1a sparse mode: only the selected K/V rows
+ * are read; survey section 1.1 for the softmax(q K^T * scale) V form).
+ *   idx        int32 [batch][num_q_heads][k_max]: token indices per (b, h); entries
+ *              < 0 or >= N_b are skipped, so any list of valid indices works, not
+ *              only one written by sparse_decode_index_topk.
+ *   k_per_seq  int32 [batch] or NULL: only the first min(k_b, k_max) entries of each
+ *              row are read (NULL reads all k_max).
+ *   softmax_scale  multiplies q . K before the softmax (1/sqrt(128) is standard).
+ *   out        fp32 [batch][num_q_heads][128]: sum_j e^{l_j - m} V_j / sum_j e^{l_j - m}
+ *              over the listed tokens; a row with no valid index gets 0.
+ */
+SDI_API int sparse_decode_attend(const sdi_kv *kv, const void *q, int32_t num_q_heads, const int32_t *idx,
+                         const int32_t *k_per_seq, int32_t k_max, float softmax_scale, float *out,
+                         void *ws, size_t ws_bytes, void *stream);
+
+SDI_API size_t sparse_decode_attend_workspace(const sdi_kv *kv, int32_t num_q_heads, int32_t k_max);
+
+/*
+ * Dense decode (paper Fig. 1a dense mode: the whole cache is read every step).
+ * Same output as sparse_decode_attend over every token j < N_b.
+ */
+SDI_API int dense_decode(const sdi_kv *kv, const void *q, int32_t num_q_heads, float softmax_scale,
+                 float *out, void *ws, size_t ws_bytes, void *stream);
+
+SDI_API size_t dense_decode_workspace(const sdi_kv *kv, int32_t num_q_heads);
+
+/* Static description of a return code (never NULL). */
+SDI_API const char *sparse_decode_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPARSE_DECODE_H */

@@ -1,0 +1,225 @@
+"""Context-sparse decode on MI355X (gfx950): exact top-k indexer, sparse gather-attend
+and a dense decode reference, over a paged bf16 KV cache.
+
+This module is a thin ctypes binding over the C ABI in include/sparse_decode.h
+(libsparse_decode.so, built in-tree by build.py).  It only marshals arguments:
+torch tensors supply device pointers and the current HIP stream; every step of
+the computation runs in the library's HIP kernels.  There is no fallback: if the
+library is missing, importing the binding's entry points raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libsparse_decode.so")
+
+HEAD_DIM = 128
+PAGE_SIZE = 16
+DEFAULT_SCALE = 1.0 / math.sqrt(HEAD_DIM)
+
+SDI_OK, SDI_ERR_NULL, SDI_ERR_SHAPE, SDI_ERR_K, SDI_ERR_WORKSPACE, SDI_ERR_HIP = 0, -1, -2, -3, -4, -5
+
+EXPORTS = (
+    "sparse_decode_index_topk", "sparse_decode_index_topk_workspace",
+    "sparse_decode_attend", "sparse_decode_attend_workspace",
+    "dense_decode", "dense_decode_workspace", "sparse_decode_strerror",
+)
+
+
+class SdiKV(ctypes.Structure):
+    """Mirror of struct sdi_kv."""
+    _fields_ = [
+        ("k_cache", ctypes.c_void_p), ("v_cache", ctypes.c_void_p),
+        ("page_table", ctypes.c_void_p), ("seq_lens", ctypes.c_void_p),
+        ("batch", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+        ("page_size", ctypes.c_int32), ("max_pages_per_seq", ctypes.c_int32), ("num_pages", ctypes.c_int32),
+        ("n_max", ctypes.c_int32),
+    ]
+
+
+class SparseDecodeError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        super().__init__(f"{where}: {strerror(code)} (status {code})")
+        self.code = code
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libsparse_decode.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None and path == LIB_PATH:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python {os.path.join(HERE, 'build.py')}`")
+    lib = ctypes.CDLL(path)
+    p, i32, sz, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.c_float
+    kvp = ctypes.POINTER(SdiKV)
+    lib.sparse_decode_index_topk.argtypes = [kvp, p, i32, p, i32, p, p, sz, p]
+    lib.sparse_decode_index_topk.restype = ctypes.c_int
+    lib.sparse_decode_index_topk_workspace.argtypes = [kvp, i32, i32]
+    lib.sparse_decode_index_topk_workspace.restype = sz
+    lib.sparse_decode_attend.argtypes = [kvp, p, i32, p, p, i32, f32, p, p, sz, p]
+    lib.sparse_decode_attend.restype = ctypes.c_int
+    lib.sparse_decode_attend_workspace.argtypes = [kvp, i32, i32]
+    lib.sparse_decode_attend_workspace.restype = sz
+    lib.dense_decode.argtypes = [kvp, p, i32, f32, p, p, sz, p]
+    lib.dense_decode.restype = ctypes.c_int
+    lib.dense_decode_workspace.argtypes = [kvp, i32]
+    lib.dense_decode_workspace.restype = sz
+    lib.sparse_decode_strerror.argtypes = [ctypes.c_int]
+    lib.sparse_decode_strerror.restype = ctypes.c_char_p
+    if path == LIB_PATH:
+        _lib = lib
+    return lib
+
+
+def strerror(code: int) -> str:
+    return load_library().sparse_decode_strerror(int(code)).decode()
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else int(t.data_ptr())
+
+
+def _stream(stream) -> Optional[int]:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _check(t, name, dtype, ndim):
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+
+
+class PagedKV:
+    """A paged bf16 KV cache on the device: k/v [pages][Hkv][16][128] (bf16), page_table
+    [B][max_pages] int32, seq_lens [B] int32, plus the host value n_max = max(seq_lens)."""
+
+    def __init__(self, k_cache, v_cache, page_table, seq_lens, n_max: Optional[int] = None):
+        import torch
+        _check(k_cache, "k_cache", torch.bfloat16, 4)
+        if v_cache is not None:
+            _check(v_cache, "v_cache", torch.bfloat16, 4)
+            if v_cache.shape != k_cache.shape:
+                raise ValueError("k_cache and v_cache shapes differ")
+        _check(page_table, "page_table", torch.int32, 2)
+        _check(seq_lens, "seq_lens", torch.int32, 1)
+        self.k_cache, self.v_cache, self.page_table, self.seq_lens = k_cache, v_cache, page_table, seq_lens
+        self.n_max = int(seq_lens.max().item()) if n_max is None else int(n_max)
+
+    @property
+    def batch(self) -> int:
+        return int(self.page_table.shape[0])
+
+    @property
+    def num_kv_heads(self) -> int:
+        return int(self.k_cache.shape[1])
+
+    def struct(self) -> SdiKV:
+        k = self.k_cache
+        return SdiKV(_ptr(k), _ptr(self.v_cache), _ptr(self.page_table), _ptr(self.seq_lens),
+                     int(self.page_table.shape[0]), int(k.shape[1]), int(k.shape[3]), int(k.shape[2]),
+                     int(self.page_table.shape[1]), int(k.shape[0]), self.n_max)
+
+
+def index_topk_workspace_bytes(kv: PagedKV, num_q_heads: int, k_max: int) -> int:
+    s = kv.struct()
+    return int(load_library().sparse_decode_index_topk_workspace(ctypes.byref(s), num_q_heads, k_max))
+
+
+def attend_workspace_bytes(kv: PagedKV, num_q_heads: int, k_max: int) -> int:
+    s = kv.struct()
+    return int(load_library().sparse_decode_attend_workspace(ctypes.byref(s), num_q_heads, k_max))
+
+
+def dense_workspace_bytes(kv: PagedKV, num_q_heads: int) -> int:
+    s = kv.struct()
+    return int(load_library().dense_decode_workspace(ctypes.byref(s), num_q_heads))
+
+
+def _workspace(nbytes: int, device, workspace):
+    import torch
+    if workspace is not None:
+        if workspace.numel() * workspace.element_size() < nbytes:
+            raise ValueError(f"workspace holds {workspace.numel() * workspace.element_size()} bytes, needs {nbytes}")
+        return workspace
+    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+
+
+def index_topk(kv: PagedKV, q, k_per_seq, k_max: int, idx_out=None, workspace=None, stream=None):
+    """Exact top-k per (b, query head): int32 [B][Hq][k_max], ascending, -1 padded."""
+    import torch
+    _check(q, "q", torch.bfloat16, 3)
+    _check(k_per_seq, "k_per_seq", torch.int32, 1)
+    B, hq, _ = q.shape
+    if idx_out is None:
+        idx_out = torch.empty((B, hq, k_max), dtype=torch.int32, device=q.device)
+    s = kv.struct()
+    lib = load_library()
+    ws = _workspace(lib.sparse_decode_index_topk_workspace(ctypes.byref(s), hq, k_max), q.device, workspace)
+    rc = lib.sparse_decode_index_topk(ctypes.byref(s), _ptr(q), hq, _ptr(k_per_seq), k_max, _ptr(idx_out),
+                                      _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+    if rc != SDI_OK:
+        raise SparseDecodeError(rc, "sparse_decode_index_topk")
+    return idx_out
+
+
+def attend(kv: PagedKV, q, idx, k_per_seq=None, softmax_scale: float = DEFAULT_SCALE, out=None,
+           workspace=None, stream=None):
+    """Softmax attention over the listed rows: fp32 [B][Hq][128]."""
+    import torch
+    _check(q, "q", torch.bfloat16, 3)
+    _check(idx, "idx", torch.int32, 3)
+    if k_per_seq is not None:
+        _check(k_per_seq, "k_per_seq", torch.int32, 1)
+    B, hq, _ = q.shape
+    k_max = int(idx.shape[2])
+    if out is None:
+        out = torch.empty((B, hq, HEAD_DIM), dtype=torch.float32, device=q.device)
+    s = kv.struct()
+    lib = load_library()
+    ws = _workspace(lib.sparse_decode_attend_workspace(ctypes.byref(s), hq, k_max), q.device, workspace)
+    rc = lib.sparse_decode_attend(ctypes.byref(s), _ptr(q), hq, _ptr(idx), _ptr(k_per_seq), k_max,
+                                  float(softmax_scale), _ptr(out), _ptr(ws), ws.numel() * ws.element_size(),
+                                  _stream(stream))
+    if rc != SDI_OK:
+        raise SparseDecodeError(rc, "sparse_decode_attend")
+    return out
+
+
+def dense(kv: PagedKV, q, softmax_scale: float = DEFAULT_SCALE, out=None, workspace=None, stream=None):
+    """Softmax attention over every cached token: fp32 [B][Hq][128]."""
+    import torch
+    _check(q, "q", torch.bfloat16, 3)
+    B, hq, _ = q.shape
+    if out is None:
+        out = torch.empty((B, hq, HEAD_DIM), dtype=torch.float32, device=q.device)
+    s = kv.struct()
+    lib = load_library()
+    ws = _workspace(lib.dense_decode_workspace(ctypes.byref(s), hq), q.device, workspace)
+    rc = lib.dense_decode(ctypes.byref(s), _ptr(q), hq, float(softmax_scale), _ptr(out), _ptr(ws),
+                          ws.numel() * ws.element_size(), _stream(stream))
+    if rc != SDI_OK:
+        raise SparseDecodeError(rc, "dense_decode")
+    return out
+
+
+def decode_step(kv: PagedKV, q, k_per_seq, k_max: int, softmax_scale: float = DEFAULT_SCALE,
+                idx_out=None, out=None, index_ws=None, attend_ws=None, stream=None):
+    """One sparse decode step: exact top-k, then attend over the selected rows."""
+    idx = index_topk(kv, q, k_per_seq, k_max, idx_out=idx_out, workspace=index_ws, stream=stream)
+    return idx, attend(kv, q, idx, k_per_seq, softmax_scale, out=out, workspace=attend_ws, stream=stream)

@@ -1,0 +1,119 @@
+// C ABI of the context-sparse decode library: argument checks, workspace sizing,
+// and the launches of the gfx950 kernels.  Every check runs before anything is
+// enqueued, so a call that returns an error has launched nothing.
+#include <limits.h>
+
+#include "../../include/sparse_decode.h"
+#include "sdi_launch.hpp"
+
+namespace {
+
+int check_kv(const sdi_kv *kv, bool need_v)
+{
+    if (!kv || !kv->k_cache || !kv->page_table || !kv->seq_lens || (need_v && !kv->v_cache)) return SDI_ERR_NULL;
+    if (kv->head_dim != 128 || kv->page_size != 16) return SDI_ERR_SHAPE;
+    if (kv->batch < 1 || kv->num_kv_heads < 1 || kv->num_pages < 1 || kv->n_max < 1) return SDI_ERR_SHAPE;
+    if (kv->batch > 65535) return SDI_ERR_SHAPE;            // grid z / y limits
+    if (kv->max_pages_per_seq < (int32_t)(((int64_t)kv->n_max + 15) / 16)) return SDI_ERR_SHAPE;
+    // cache rows are addressed with 32-bit row numbers
+    if ((int64_t)kv->num_pages * kv->num_kv_heads * 16 > (int64_t)INT_MAX) return SDI_ERR_SHAPE;
+    return SDI_OK;
+}
+
+int check_heads(const sdi_kv *kv, int32_t num_q_heads)
+{
+    if (num_q_heads < 1 || num_q_heads % kv->num_kv_heads != 0) return SDI_ERR_SHAPE;
+    if (num_q_heads > 65535) return SDI_ERR_SHAPE;          // grid x / y limits
+    if ((int64_t)kv->batch * num_q_heads > (int64_t)INT_MAX / 2) return SDI_ERR_SHAPE;
+    return SDI_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? SDI_OK : SDI_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+size_t sparse_decode_index_topk_workspace(const sdi_kv *kv, int32_t num_q_heads, int32_t k_max)
+{
+    (void)k_max;
+    if (!kv || kv->batch < 1 || kv->n_max < 1 || num_q_heads < 1) return 0;
+    return sdi::index_topk_workspace_bytes(kv->batch, num_q_heads, kv->n_max);
+}
+
+size_t sparse_decode_attend_workspace(const sdi_kv *kv, int32_t num_q_heads, int32_t k_max)
+{
+    if (!kv || kv->batch < 1 || num_q_heads < 1 || k_max < 1) return 0;
+    return sdi::attend_workspace_bytes(kv->batch, num_q_heads, k_max);
+}
+
+size_t dense_decode_workspace(const sdi_kv *kv, int32_t num_q_heads)
+{
+    if (!kv || kv->batch < 1 || kv->n_max < 1 || num_q_heads < 1) return 0;
+    return sdi::dense_workspace_bytes(kv->batch, num_q_heads, kv->n_max);
+}
+
+int sparse_decode_index_topk(const sdi_kv *kv, const void *q, int32_t num_q_heads, const int32_t *k_per_seq,
+                             int32_t k_max, int32_t *idx_out, void *ws, size_t ws_bytes, void *stream)
+{
+    int rc = check_kv(kv, false);
+    if (rc) return rc;
+    if (!q || !k_per_seq || !idx_out) return SDI_ERR_NULL;
+    if ((rc = check_heads(kv, num_q_heads))) return rc;
+    if (k_max < 1) return SDI_ERR_K;
+    const size_t need = sparse_decode_index_topk_workspace(kv, num_q_heads, k_max);
+    if (need > 0 && !ws) return SDI_ERR_NULL;
+    if (ws_bytes < need) return SDI_ERR_WORKSPACE;
+    sdi::IndexArgs a{kv->k_cache, kv->page_table, kv->seq_lens, kv->batch, kv->num_kv_heads,
+                     kv->max_pages_per_seq, kv->n_max, q, num_q_heads, k_per_seq, k_max, idx_out, ws};
+    return hip_status(sdi::launch_index_topk(a, (hipStream_t)stream));
+}
+
+int sparse_decode_attend(const sdi_kv *kv, const void *q, int32_t num_q_heads, const int32_t *idx,
+                         const int32_t *k_per_seq, int32_t k_max, float softmax_scale, float *out, void *ws,
+                         size_t ws_bytes, void *stream)
+{
+    int rc = check_kv(kv, true);
+    if (rc) return rc;
+    if (!q || !idx || !out) return SDI_ERR_NULL;
+    if ((rc = check_heads(kv, num_q_heads))) return rc;
+    if (k_max < 1) return SDI_ERR_K;
+    const size_t need = sparse_decode_attend_workspace(kv, num_q_heads, k_max);
+    if (need > 0 && !ws) return SDI_ERR_NULL;
+    if (ws_bytes < need) return SDI_ERR_WORKSPACE;
+    sdi::AttendArgs a{kv->k_cache, kv->v_cache, kv->page_table, kv->seq_lens, kv->batch, kv->num_kv_heads,
+                      kv->max_pages_per_seq, kv->n_max, q, num_q_heads, idx, k_per_seq, k_max, softmax_scale,
+                      out, ws};
+    return hip_status(sdi::launch_attend(a, (hipStream_t)stream));
+}
+
+int dense_decode(const sdi_kv *kv, const void *q, int32_t num_q_heads, float softmax_scale, float *out, void *ws,
+                 size_t ws_bytes, void *stream)
+{
+    int rc = check_kv(kv, true);
+    if (rc) return rc;
+    if (!q || !out) return SDI_ERR_NULL;
+    if ((rc = check_heads(kv, num_q_heads))) return rc;
+    const size_t need = dense_decode_workspace(kv, num_q_heads);
+    if (need > 0 && !ws) return SDI_ERR_NULL;
+    if (ws_bytes < need) return SDI_ERR_WORKSPACE;
+    sdi::AttendArgs a{kv->k_cache, kv->v_cache, kv->page_table, kv->seq_lens, kv->batch, kv->num_kv_heads,
+                      kv->max_pages_per_seq, kv->n_max, q, num_q_heads, nullptr, nullptr, 0, softmax_scale,
+                      out, ws};
+    return hip_status(sdi::launch_dense(a, (hipStream_t)stream));
+}
+
+const char *sparse_decode_strerror(int code)
+{
+    switch (code) {
+    case SDI_OK: return "ok";
+    case SDI_ERR_NULL: return "a required pointer is NULL";
+    case SDI_ERR_SHAPE: return "unsupported shape (head_dim must be 128, page_size 16, q heads a multiple of kv heads, sizes >= 1)";
+    case SDI_ERR_K: return "k_max must be at least 1";
+    case SDI_ERR_WORKSPACE: return "workspace smaller than the size the *_workspace() query returns";
+    case SDI_ERR_HIP: return "a HIP kernel launch failed";
+    default: return "unknown sparse_decode status";
+    }
+}
+
+}  // extern "C"

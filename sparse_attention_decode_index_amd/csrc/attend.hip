@@ -1,0 +1,231 @@
+// Sparse gather-attend for the context-sparse decode step (gfx950).
+//
+// The sparse decode mode of the context-sparsity paper (Fig. 1a) reads only the
+// k selected K/V rows of each (sequence, query head); the selections differ per
+// token, per query and per head (paper section 1), so each query head gathers its
+// own rows and there is no shared contraction for MFMA: this is a matrix-vector
+// product on the vector ALU.  Softmax over the selected rows uses the running
+// (max, sum, accumulator) merge of FlashAttention's tiling (survey page, section
+// 5.1) in fp32, split over chunks of the index list, and the chunk partials are
+// combined by merge_kernel with a log-sum-exp merge.
+//
+// Work decomposition: a workgroup of 4 waves takes 256 consecutive entries of one
+// (b, h) index row; each wave takes 64.  Inside a wave, each group of 16 lanes owns
+// one gathered row at a time (16 lanes x 16 B = the 256 B row, one 128-bit load
+// per lane for K and one for V), 8 rows per group are in flight at once, and each
+// group keeps its own running softmax state; the 4 groups, then the 4 waves, are
+// merged at the end.
+#include "sdi_device.hpp"
+#include "sdi_launch.hpp"
+
+namespace sdi {
+
+constexpr int kAttWaves = 4;
+constexpr int kAttPerWave = 64;
+constexpr int kAttPerBlock = kAttWaves * kAttPerWave;   // 256 index entries per workgroup
+constexpr int kAttBatch = 8;                            // rows per 16-lane group in flight
+constexpr float kLog2e = 1.4426950408889634f;
+
+// grid (splits, num_q_heads, batch); 256 threads.
+__global__ __launch_bounds__(kAttWaves * 64) void attend_kernel(
+    const uint16_t *__restrict__ kc, const uint16_t *__restrict__ vc, const int32_t *__restrict__ page_table,
+    const int32_t *__restrict__ seq_lens, const uint16_t *__restrict__ q, const int32_t *__restrict__ idx,
+    const int32_t *__restrict__ k_per_seq, int num_q_heads, int num_kv_heads, int group, int max_pages, int k_max,
+    float scale_log2, int splits, float *__restrict__ part_ml, float *__restrict__ part_acc,
+    float *__restrict__ out)
+{
+    __shared__ float red_acc[kAttWaves][kHeadDim];
+    __shared__ float red_ml[kAttWaves][2];
+    const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int64_t bh = (int64_t)b * num_q_heads + h;
+    const int g = h / group;
+    const int n = seq_lens[b];
+    int kk = k_per_seq ? min(k_per_seq[b], k_max) : k_max;
+    if (kk < 0) kk = 0;
+    const int i0 = split * kAttPerBlock;
+    if (i0 >= kk) {                          // nothing listed in this chunk
+        if (splits == 1 && threadIdx.x < kHeadDim) out[bh * kHeadDim + threadIdx.x] = 0.f;
+        return;                              // (chunks past k are never merged)
+    }
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int grp = lane >> 4, sub = lane & 15;
+
+    float qf[8];
+    {
+        const u32x4 w = *(const u32x4 *)(q + bh * kHeadDim + sub * 8);
+        unpack8(w, qf);
+#pragma unroll
+        for (int d = 0; d < 8; ++d) qf[d] *= scale_log2;
+    }
+
+    // Each lane resolves one index of the wave's 64 to a cache row number (-1 = skip).
+    int my_row = -1;
+    {
+        const int i = i0 + wave * kAttPerWave + lane;
+        if (i < kk) {
+            const int j = idx[bh * k_max + i];
+            if (j >= 0 && j < n) {
+                const int page = page_table[(int64_t)b * max_pages + (j >> 4)];
+                my_row = (page * num_kv_heads + g) * kPage + (j & 15);
+            }
+        }
+    }
+
+    float m = -INFINITY, l = 0.f, acc[8];
+#pragma unroll
+    for (int d = 0; d < 8; ++d) acc[d] = 0.f;
+
+#pragma unroll
+    for (int r0 = 0; r0 < kAttPerWave / 4; r0 += kAttBatch) {
+        u32x4 kw[kAttBatch], vw[kAttBatch];
+        int rows[kAttBatch];
+#pragma unroll
+        for (int r = 0; r < kAttBatch; ++r) {
+            rows[r] = __shfl(my_row, (r0 + r) * 4 + grp, 64);
+            kw[r] = u32x4{0u, 0u, 0u, 0u};
+            vw[r] = u32x4{0u, 0u, 0u, 0u};
+            if (rows[r] >= 0) {
+                const int64_t off = (int64_t)rows[r] * kHeadDim + sub * 8;
+                kw[r] = *(const u32x4 *)(kc + off);
+                vw[r] = *(const u32x4 *)(vc + off);
+            }
+        }
+        float x[kAttBatch];
+        float bmax = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < kAttBatch; ++r) {
+            float kf[8];
+            unpack8(kw[r], kf);
+            float s = 0.f;
+#pragma unroll
+            for (int d = 0; d < 8; ++d) s = fmaf(qf[d], kf[d], s);
+            s = row16_sum(s);
+            x[r] = rows[r] >= 0 ? s : -INFINITY;
+            bmax = fmaxf(bmax, x[r]);
+        }
+        const float m_new = fmaxf(m, bmax);
+        if (m_new != -INFINITY) {
+            const float alpha = fast_exp2(m - m_new);
+            l *= alpha;
+#pragma unroll
+            for (int d = 0; d < 8; ++d) acc[d] *= alpha;
+#pragma unroll
+            for (int r = 0; r < kAttBatch; ++r) {
+                const float p = fast_exp2(x[r] - m_new);
+                float vf[8];
+                unpack8(vw[r], vf);
+                l += p;
+#pragma unroll
+                for (int d = 0; d < 8; ++d) acc[d] = fmaf(p, vf[d], acc[d]);
+            }
+            m = m_new;
+        }
+    }
+
+    // Merge the 4 groups of this wave (lanes xor 16 and xor 32 hold the same dims).
+    float M = fmaxf(m, __shfl_xor(m, 16, 64));
+    M = fmaxf(M, __shfl_xor(M, 32, 64));
+    const float f = (M == -INFINITY) ? 0.f : fast_exp2(m - M);
+    l *= f;
+    l += __shfl_xor(l, 16, 64);
+    l += __shfl_xor(l, 32, 64);
+#pragma unroll
+    for (int d = 0; d < 8; ++d) {
+        float a = acc[d] * f;
+        a += __shfl_xor(a, 16, 64);
+        a += __shfl_xor(a, 32, 64);
+        acc[d] = a;
+    }
+    if (grp == 0) {
+#pragma unroll
+        for (int d = 0; d < 8; ++d) red_acc[wave][sub * 8 + d] = acc[d];
+        if (sub == 0) { red_ml[wave][0] = M; red_ml[wave][1] = l; }
+    }
+    __syncthreads();
+
+    // Merge the 4 waves; thread t < 128 owns output dim t.
+    if (threadIdx.x < kHeadDim) {
+        const int t = threadIdx.x;
+        float Mw = red_ml[0][0];
+#pragma unroll
+        for (int w = 1; w < kAttWaves; ++w) Mw = fmaxf(Mw, red_ml[w][0]);
+        float L = 0.f, A = 0.f;
+#pragma unroll
+        for (int w = 0; w < kAttWaves; ++w) {
+            const float fw = (Mw == -INFINITY) ? 0.f : fast_exp2(red_ml[w][0] - Mw);
+            L += fw * red_ml[w][1];
+            A += fw * red_acc[w][t];
+        }
+        if (splits == 1) {
+            out[bh * kHeadDim + t] = L > 0.f ? A / L : 0.f;
+        } else {
+            const int64_t ps = bh * splits + split;
+            part_acc[ps * kHeadDim + t] = A;
+            if (t == 0) { part_ml[ps * 2] = Mw; part_ml[ps * 2 + 1] = L; }
+        }
+    }
+}
+
+// Log-sum-exp merge of per-chunk partials (m, l, acc[128]) of each (b, h).
+// live chunks = ceil(count / per_chunk) with count = min(k_b, k_max) (sparse) or N_b
+// (dense).  grid (num_q_heads, batch); 128 threads, thread t owns dim t.
+__global__ __launch_bounds__(kHeadDim) void merge_kernel(const float *__restrict__ part_ml,
+                                                         const float *__restrict__ part_acc, int splits,
+                                                         int per_chunk, const int32_t *__restrict__ counts,
+                                                         int count_cap, int num_q_heads, float *__restrict__ out)
+{
+    const int h = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
+    const int64_t bh = (int64_t)b * num_q_heads + h;
+    int cnt = counts ? min(counts[b], count_cap) : count_cap;
+    if (cnt < 0) cnt = 0;
+    const int live = min(splits, (cnt + per_chunk - 1) / per_chunk);
+    float M = -INFINITY;
+    for (int s = 0; s < live; ++s) M = fmaxf(M, part_ml[(bh * splits + s) * 2]);
+    float L = 0.f, A = 0.f;
+    if (M != -INFINITY) {
+        for (int s = 0; s < live; ++s) {
+            const int64_t ps = bh * splits + s;
+            const float f = fast_exp2(part_ml[ps * 2] - M);
+            L += f * part_ml[ps * 2 + 1];
+            A += f * part_acc[ps * kHeadDim + t];
+        }
+    }
+    out[bh * kHeadDim + t] = L > 0.f ? A / L : 0.f;
+}
+
+int attend_splits(int k_max) { return (k_max + kAttPerBlock - 1) / kAttPerBlock; }
+
+size_t attend_workspace_bytes(int batch, int num_q_heads, int k_max)
+{
+    const int splits = attend_splits(k_max);
+    if (splits <= 1) return 0;
+    return (size_t)batch * num_q_heads * splits * (kHeadDim + 2) * sizeof(float);
+}
+
+hipError_t launch_merge(const float *part_ml, const float *part_acc, int splits, int per_chunk,
+                        const int32_t *counts, int count_cap, int batch, int num_q_heads, float *out,
+                        hipStream_t stream)
+{
+    hipLaunchKernelGGL(merge_kernel, dim3(num_q_heads, batch), dim3(kHeadDim), 0, stream, part_ml, part_acc, splits,
+                       per_chunk, counts, count_cap, num_q_heads, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_attend(const AttendArgs &a, hipStream_t stream)
+{
+    const int group = a.num_q_heads / a.num_kv_heads;
+    const int splits = attend_splits(a.k_max);
+    const size_t bhs = (size_t)a.batch * a.num_q_heads * splits;
+    float *part_acc = (float *)a.ws;
+    float *part_ml = splits > 1 ? part_acc + bhs * kHeadDim : nullptr;
+    hipLaunchKernelGGL(attend_kernel, dim3(splits, a.num_q_heads, a.batch), dim3(kAttWaves * 64), 0, stream,
+                       (const uint16_t *)a.k_cache, (const uint16_t *)a.v_cache, a.page_table, a.seq_lens,
+                       (const uint16_t *)a.q, a.idx, a.k_per_seq, a.num_q_heads, a.num_kv_heads, group, a.max_pages,
+                       a.k_max, a.scale * kLog2e, splits, part_ml, part_acc, a.out);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || splits == 1) return e;
+    return launch_merge(part_ml, part_acc, splits, kAttPerBlock, a.k_per_seq, a.k_max, a.batch, a.num_q_heads,
+                        a.out, stream);
+}
+
+}  // namespace sdi

@@ -1,0 +1,55 @@
+// Host-side launchers of the gfx950 kernels (internal to the library).
+// Arguments are already validated by the C ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+namespace sdi {
+
+struct IndexArgs {
+    const void *k_cache;
+    const int32_t *page_table, *seq_lens;
+    int batch, num_kv_heads, max_pages, n_max;
+    const void *q;
+    int num_q_heads;
+    const int32_t *k_per_seq;
+    int k_max;
+    int32_t *idx_out;
+    void *ws;
+};
+
+struct AttendArgs {
+    const void *k_cache, *v_cache;
+    const int32_t *page_table, *seq_lens;
+    int batch, num_kv_heads, max_pages, n_max;
+    const void *q;
+    int num_q_heads;
+    const int32_t *idx;        // NULL for dense
+    const int32_t *k_per_seq;  // may be NULL
+    int k_max;
+    float scale;
+    float *out;
+    void *ws;
+};
+
+size_t index_topk_key_stride(int n_max);
+size_t index_topk_workspace_bytes(int batch, int num_q_heads, int n_max);
+hipError_t launch_index_topk(const IndexArgs &a, hipStream_t stream);
+
+int attend_splits(int k_max);
+size_t attend_workspace_bytes(int batch, int num_q_heads, int k_max);
+hipError_t launch_attend(const AttendArgs &a, hipStream_t stream);
+
+hipError_t launch_merge(const float *part_ml, const float *part_acc, int splits, int per_chunk,
+                        const int32_t *counts, int count_cap, int batch, int num_q_heads, float *out,
+                        hipStream_t stream);
+
+int dense_splits(int n_max);
+size_t dense_workspace_bytes(int batch, int num_q_heads, int n_max);
+hipError_t launch_dense(const AttendArgs &a, hipStream_t stream);
+
+}  // namespace sdi

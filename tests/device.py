@@ -1,0 +1,51 @@
+"""Moving host workloads (synth.Workload or helpers.TinyCase) onto the GPU."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import sparse_attention_decode_index_amd as sdi
+
+
+def bf16_tensor(bits: np.ndarray, device="cuda"):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(device).view(torch.bfloat16)
+
+
+def i32_tensor(a, device="cuda"):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(device)
+
+
+class DeviceCase:
+    """Device copies of a paged cache + queries."""
+
+    def __init__(self, k_cache, v_cache, page_table, seq_lens, q, device="cuda"):
+        self.k = bf16_tensor(k_cache, device)
+        self.v = bf16_tensor(v_cache, device)
+        self.pt = i32_tensor(page_table, device)
+        self.sl = i32_tensor(seq_lens, device)
+        self.q = bf16_tensor(q, device)
+        self.kv = sdi.PagedKV(self.k, self.v, self.pt, self.sl, n_max=int(np.max(seq_lens)))
+
+    @classmethod
+    def of_workload(cls, wl, device="cuda"):
+        return cls(wl.k_cache, wl.v_cache, wl.page_table, wl.seq_lens, wl.q, device)
+
+    @classmethod
+    def of_tiny(cls, case, device="cuda"):
+        return cls(case.k_cache, case.v_cache, case.page_table, case.lens, case.q, device)
+
+    def index(self, k_per_seq, k_max):
+        idx = sdi.index_topk(self.kv, self.q, i32_tensor(k_per_seq), k_max)
+        torch.cuda.synchronize()
+        return idx.cpu().numpy()
+
+    def attend(self, idx, k_per_seq=None, scale=sdi.DEFAULT_SCALE):
+        kp = None if k_per_seq is None else i32_tensor(k_per_seq)
+        out = sdi.attend(self.kv, self.q, i32_tensor(idx), kp, scale)
+        torch.cuda.synchronize()
+        return out.cpu().numpy()
+
+    def dense(self, scale=sdi.DEFAULT_SCALE):
+        out = sdi.dense(self.kv, self.q, scale)
+        torch.cuda.synchronize()
+        return out.cpu().numpy()

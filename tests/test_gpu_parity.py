@@ -1,0 +1,265 @@
+"""GPU parity: the HIP library through its C ABI against the fp64 oracle.
+
+Sizes are ones the oracle finishes in seconds yet span several score chunks
+(1024 tokens), several attend chunks (256 indices) and a ragged tail; the
+full-size decode layer that the benchmark times is checked on sampled
+sequences.  Comparison rules are in tests/parity.py.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from helpers import TinyCase, bf16_round, random_case
+from parity import check_close, check_indices
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    from device import DeviceCase, i32_tensor
+    import sparse_attention_decode_index_amd as sdi
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def run_and_check(dev, cache, q, k_per_seq, k_max, strict=False, check_dense=True, tag=""):
+    """Index + attend + dense on the GPU, each against the oracle.  Returns GPU results."""
+    _say(f"[case] {tag} B={cache.batch} Hq={q.shape[1]} Hkv={cache.num_kv_heads} "
+         f"N={list(cache.sl)[:4]} k={list(k_per_seq)[:4]} k_max={k_max}")
+    s = oracle.scores(cache, q)
+    ora_idx, kth = oracle.topk(np.nan_to_num(s, nan=-np.inf), cache.sl, k_per_seq, k_max)
+    gpu_idx = dev.index(k_per_seq, k_max)
+    swaps = check_indices(gpu_idx, ora_idx, s, kth, cache.sl, k_per_seq, strict=strict)
+    # attend on the oracle's list (both sides see the same rows)
+    ora_out = oracle.attend(cache, q, ora_idx)
+    gpu_out = dev.attend(ora_idx, k_per_seq)
+    check_close(gpu_out, ora_out, what=f"{tag} attend(oracle idx)")
+    # end to end: the GPU's own (validated) list on both sides
+    e2e = dev.attend(gpu_idx, k_per_seq)
+    check_close(e2e, oracle.attend(cache, q, gpu_idx), what=f"{tag} attend(gpu idx)")
+    dn = None
+    if check_dense:
+        dn = dev.dense()
+        check_close(dn, oracle.dense(cache, q), what=f"{tag} dense")
+    return gpu_idx, e2e, dn, swaps
+
+
+# ------------------------------------------------------------------------ configurations
+
+def test_config1_full_size():
+    wl = synth.config(1)
+    dev = DeviceCase.of_workload(wl)
+    run_and_check(dev, oracle.Cache.of(wl), wl.q, wl.k_per_seq(), wl.k_max(), tag="C1")
+
+
+@pytest.mark.parametrize("cfg,kw", [
+    (2, dict(n=4100, batch=2)),
+    (3, dict(n=3001, batch=2)),
+    (5, dict(n=6000, batch=6, steps=1)),
+], ids=["C2-small", "C3-small", "C5-small"])
+def test_config_small(cfg, kw):
+    wl = synth.config(cfg, **kw)
+    dev = DeviceCase.of_workload(wl)
+    run_and_check(dev, oracle.Cache.of(wl), wl.q, wl.k_per_seq(), wl.k_max(), tag=f"C{cfg}-small")
+
+
+def _append_on_device(dev, rows):
+    tok, pages, slots, kr, vr = rows
+    from device import bf16_tensor
+    p = torch.from_numpy(pages).cuda()
+    s = torch.from_numpy(slots).cuda()
+    dev.k[p, :, s, :] = bf16_tensor(kr)
+    dev.v[p, :, s, :] = bf16_tensor(vr)
+    dev.sl += 1
+
+
+@pytest.mark.parametrize("cfg,kw,ratios", [
+    (4, dict(n=5000, batch=2, steps=3), (100, 50, 20, 1)),
+    (5, dict(n=6000, batch=6, steps=3), (50,)),
+], ids=["C4-small-sweep", "C5-small-growth"])
+def test_multi_step_growth(cfg, kw, ratios):
+    """Cache growth by one token per step (appended on the device with plain copies);
+    every step is checked, for each sparsity ratio (k = N runs dense as well)."""
+    wl = synth.config(cfg, **kw)
+    dev = DeviceCase.of_workload(wl)
+    for step in range(wl.steps):
+        if step > 0:
+            rows = wl.advance()                          # host copy for the oracle
+            _append_on_device(dev, rows)
+            dev.q.copy_(torch.from_numpy(wl.q.view(np.int16)).cuda().view(torch.bfloat16))
+            dev.kv = sdi.PagedKV(dev.k, dev.v, dev.pt, dev.sl, n_max=wl.n_max)
+        cache = oracle.Cache.of(wl)
+        for r in ratios:
+            rule = synth.k_ceil(r) if cfg == 5 else synth.k_half_up(r)
+            kps = rule(wl.seq_lens)
+            gidx, e2e, dn, _ = run_and_check(dev, cache, wl.q, kps, int(kps.max()), check_dense=(r == 1 or r == ratios[0]),
+                                             tag=f"C{cfg} step{step} N/{r}")
+            if r == 1:                                   # k = N: the sparse path equals dense
+                check_close(e2e, dn, what="k=N sparse vs dense")
+
+
+# ------------------------------------------------------------------------ edge cases
+
+@pytest.mark.parametrize("hq,hkv", [(3, 3), (4, 2), (16, 2), (10, 2), (32, 2), (64, 2)],
+                         ids=["G1", "G2", "G8", "G5", "G16", "G32-two-head-blocks"])
+def test_group_sizes(hq, hkv):
+    rng = np.random.default_rng(hq * 100 + hkv)
+    case = random_case(rng, batch=2, hq=hq, hkv=hkv, lens=[37, 1300], layout="shuffled")
+    dev = DeviceCase.of_tiny(case)
+    cache = oracle.Cache(case.k_cache, case.v_cache, case.page_table, case.lens)
+    run_and_check(dev, cache, case.q, np.array([5, 300], np.int32), 300, tag=f"G{hq // hkv}")
+
+
+@pytest.mark.parametrize("lens,kvec,k_max", [
+    ([1, 5, 16, 17], [1, 1, 1, 1], 1),                  # k = 1, tiny contexts
+    ([1, 5, 16, 17], [3, 9, 40, 17], 40),               # k >= N clamps to N, padding
+    ([2500, 1000, 3333], [2500, 7, 999], 2600),         # k = N, ragged k
+    ([4096, 2049], [4000, 2049], 4096),                 # k close to N
+    ([9000], [8500], 8500),                              # k beyond the attend chunk count
+], ids=["k1", "k-ge-N", "ragged-k", "k-near-N", "big-k"])
+def test_k_edges(lens, kvec, k_max):
+    rng = np.random.default_rng(len(lens) * 7 + k_max)
+    case = random_case(rng, batch=len(lens), hq=8, hkv=2, lens=lens, layout="fragmented")
+    dev = DeviceCase.of_tiny(case)
+    cache = oracle.Cache(case.k_cache, case.v_cache, case.page_table, case.lens)
+    run_and_check(dev, cache, case.q, np.array(kvec, np.int32), k_max, tag="k-edge")
+
+
+def test_k1_returns_argmax_row_exactly():
+    rng = np.random.default_rng(5)
+    case = random_case(rng, batch=2, hq=4, hkv=1, lens=[700, 2000], integer=True, lo=-3, hi=3)
+    dev = DeviceCase.of_tiny(case)
+    cache = oracle.Cache(case.k_cache, case.v_cache, case.page_table, case.lens)
+    kv = np.array([1, 1], np.int32)
+    gidx = dev.index(kv, 1)
+    s = oracle.scores(cache, case.q)
+    oidx, _ = oracle.topk(np.nan_to_num(s, nan=-np.inf), case.lens, kv, 1)
+    assert np.array_equal(gidx, oidx)
+    out = dev.attend(gidx, kv)
+    for b in range(2):
+        for h in range(4):
+            assert np.array_equal(out[b, h], case.v_f[b][0][gidx[b, h, 0]].astype(np.float32))
+
+
+def test_integer_inputs_strict():
+    """Small-integer q and K make every fp32 score exact: the selection must match
+    the oracle exactly, ties included."""
+    rng = np.random.default_rng(6)
+    case = random_case(rng, batch=3, hq=8, hkv=2, lens=[3000, 1111, 2048], integer=True, lo=-1, hi=1)
+    dev = DeviceCase.of_tiny(case)
+    cache = oracle.Cache(case.k_cache, case.v_cache, case.page_table, case.lens)
+    run_and_check(dev, cache, case.q, np.array([60, 500, 2047], np.int32), 2047, strict=True, tag="int")
+
+
+def test_uniform_keys_take_first_indices():
+    rng = np.random.default_rng(7)
+    n = [1500, 777]
+    krow = bf16_round(rng.standard_normal(128))
+    k = [np.broadcast_to(krow, (2, x, 128)).copy() for x in n]
+    v = [bf16_round(rng.standard_normal((2, x, 128))) for x in n]
+    case = TinyCase(k, v, bf16_round(rng.standard_normal((2, 8, 128))))
+    dev = DeviceCase.of_tiny(case)
+    kv = np.array([300, 40], np.int32)
+    gidx = dev.index(kv, 300)
+    assert np.array_equal(gidx[0, :, :300], np.broadcast_to(np.arange(300), (8, 300)))
+    assert np.array_equal(gidx[1, :, :40], np.broadcast_to(np.arange(40), (8, 40)))
+    assert np.all(gidx[1, :, 40:] == -1)
+    out = dev.attend(gidx, kv)
+    check_close(out[0], np.broadcast_to(v[0][:, :300].mean(1).repeat(4, 0), (8, 128)), what="uniform keys b0")
+    check_close(out[1], np.broadcast_to(v[1][:, :40].mean(1).repeat(4, 0), (8, 128)), what="uniform keys b1")
+
+
+def test_one_hot_key():
+    rng = np.random.default_rng(8)
+    n, m, jstar, c = 3000, 40, 2222, 4.0
+    q = bf16_round(rng.standard_normal((1, 4, 128)))
+    q[0, :, m] = [1.5, 0.75, -1.0, 2.0]
+    k = np.zeros((1, n, 128))
+    k[0, jstar, m] = c
+    v = bf16_round(rng.standard_normal((1, n, 128)))
+    case = TinyCase([k], [v], q)
+    dev = DeviceCase.of_tiny(case)
+    kk = 20
+    gidx = dev.index(np.array([kk], np.int32), kk)
+    for h in range(4):
+        want = sorted([jstar] + list(range(kk - 1))) if q[0, h, m] > 0 else list(range(kk))
+        assert list(gidx[0, h]) == want, h
+    cache = oracle.Cache(case.k_cache, case.v_cache, case.page_table, case.lens)
+    check_close(dev.attend(gidx), oracle.attend(cache, case.q, gidx), what="one-hot attend")
+
+
+def test_attend_accepts_any_index_list():
+    """-1 holes anywhere, out-of-range entries skipped, k_per_seq omitted."""
+    rng = np.random.default_rng(9)
+    case = random_case(rng, batch=2, hq=4, hkv=1, lens=[900, 3000])
+    dev = DeviceCase.of_tiny(case)
+    cache = oracle.Cache(case.k_cache, case.v_cache, case.page_table, case.lens)
+    k_max = 700
+    idx = np.full((2, 4, k_max), -1, np.int32)
+    for b in range(2):
+        for h in range(4):
+            m = int(rng.integers(0, k_max))
+            idx[b, h, rng.choice(k_max, size=m, replace=False)] = rng.choice(case.lens[b], size=m, replace=False)
+    idx[0, 0, :] = -1                                      # an empty row gives 0
+    idx[1, 1, 5] = 5000                                    # beyond N_b: skipped
+    gpu = dev.attend(idx, None)
+    idx_o = np.where(idx >= case.lens[:, None, None], -1, idx)
+    check_close(gpu, oracle.attend(cache, case.q, idx_o), what="holes")
+    assert np.all(gpu[0, 0] == 0)
+
+
+def test_layout_invariance_and_determinism():
+    rng = np.random.default_rng(10)
+    base = random_case(rng, batch=3, hq=8, hkv=2, lens=[2000, 333, 4100], layout="contiguous")
+    kv = np.array([40, 333, 82], np.int32)
+    res = []
+    for layout, seed in (("contiguous", 1), ("shuffled", 2), ("fragmented", 3), ("shuffled", 2)):
+        case = TinyCase(base.k_f, base.v_f, base.q_f, layout=layout, seed=seed)
+        dev = DeviceCase.of_tiny(case)
+        gidx = dev.index(kv, 333)
+        res.append((gidx, dev.attend(gidx, kv), dev.dense()))
+    for other in res[1:]:
+        for a, b in zip(res[0], other):
+            assert np.array_equal(a, b)
+
+
+def test_workspace_too_small_is_rejected():
+    wl = synth.config(1)
+    dev = DeviceCase.of_workload(wl)
+    need = sdi.index_topk_workspace_bytes(dev.kv, 4, 82)
+    ws = torch.empty(need - 1, dtype=torch.uint8, device="cuda")
+    with pytest.raises(ValueError):
+        sdi.index_topk(dev.kv, dev.q, i32_tensor(wl.k_per_seq()), 82, workspace=ws)
+
+
+# ------------------------------------------------------------------------ full size, sampled
+
+@pytest.mark.parametrize("cfg,sample", [(2, [0, 5]), (3, [2])], ids=["C2-full", "C3-full"])
+def test_full_size_sampled(cfg, sample):
+    """The full decode layer in the benchmark's launch configuration; the oracle checks
+    every head of the sampled sequences, and properties are checked for every row."""
+    wl = synth.config(cfg)
+    dev = DeviceCase.of_workload(wl)
+    kps = wl.k_per_seq()
+    k_max = wl.k_max()
+    _say(f"[case] C{cfg} full size: index/attend/dense on the GPU")
+    gidx = dev.index(kps, k_max)
+    out = dev.attend(gidx, kps)
+    dn = dev.dense()
+    for b in range(wl.batch):                               # properties on every row
+        for h in range(wl.num_q_heads):
+            row = gidx[b, h]
+            assert np.all(np.diff(row[:kps[b]]) > 0) and row[0] >= 0 and row[kps[b] - 1] < wl.seq_lens[b]
+            if cfg == 2:
+                assert set(wl.meta["planted_positions"][(b, h // 4)]) <= set(row.tolist())
+    sub = np.array(sample)
+    cache = oracle.Cache(wl.k_cache, wl.v_cache, wl.page_table[sub], wl.seq_lens[sub], wl.num_kv_heads)
+    q = wl.q[sub]
+    s = oracle.scores(cache, q)
+    oidx, kth = oracle.topk(s, cache.sl, kps[sub], k_max)
+    check_indices(gidx[sub], oidx, s, kth, cache.sl, kps[sub])
+    check_close(out[sub], oracle.attend(cache, q, gidx[sub]), what=f"C{cfg} attend")
+    check_close(dn[sub], oracle.dense(cache, q), what=f"C{cfg} dense")
