@@ -41,6 +41,8 @@ def parse_args():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--cold", action="store_true", help="also time each launch group after a 1 GiB cache flush")
+    ap.add_argument("--mode", choices=("graph", "eager"), default="graph",
+                    help="replay captured HIP graphs (default) or launch eagerly from Python")
     return ap.parse_args()
 
 
@@ -171,36 +173,92 @@ def main():
         if ev is not None:
             ev[2].record(stream)
 
+    def timed_graph(body, reps, count):
+        """Capture `count` calls of body(j) into one HIP graph, replay it `reps` times
+        back to back between two events; returns (seconds per call, wall seconds)."""
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=cap_stream):
+            for j in range(count):
+                body(j)
+        for _ in range(2):
+            graph.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record()
+        for _ in range(reps):
+            graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        return e0.elapsed_time(e1) * 1e-3 / (reps * count), wall
+
+    def index_only(s):
+        kv, q, kps = step_args(s)
+        sdi.index_topk(kv, q, kps, k_max, idx_out=idx, workspace=ws_index, stream=torch.cuda.current_stream())
+
+    def attend_only(s):
+        kv, q, kps = step_args(s)
+        sdi.attend(kv, q, idx, kps, out=out, workspace=ws_attend, stream=torch.cuda.current_stream())
+
+    def dense_only(s):
+        kv, q, _ = step_args(s)
+        sdi.dense(kv, q, out=out, workspace=ws_dense, stream=torch.cuda.current_stream())
+
+    def full_step(s):
+        kv, q, kps = step_args(s)
+        j = s % n_q
+        if growth and j > 0:                              # a0: append this step's token (plain copies)
+            pg, sl_, kr, vr = appends[j - 1]
+            k_cache[pg, :, sl_, :] = kr
+            v_cache[pg, :, sl_, :] = vr
+        st = torch.cuda.current_stream()
+        sdi.index_topk(kv, q, kps, k_max, idx_out=idx, workspace=ws_index, stream=st)
+        sdi.attend(kv, q, idx, kps, out=out, workspace=ws_attend, stream=st)
+
     for s in range(args.warmup):
         run_step(s)
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    t0 = time.perf_counter()
-    for s in range(args.steps):
-        run_step(args.warmup + s, evs[s])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    t_index = np.array([e[0].elapsed_time(e[1]) for e in evs]) * 1e-3
-    t_attend = np.array([e[1].elapsed_time(e[2]) for e in evs]) * 1e-3
-    t_step_gpu = evs[0][0].elapsed_time(evs[-1][2]) * 1e-3 / args.steps if args.steps > 1 else wall
+    if args.mode == "graph":
+        # steps are replayed from one captured graph of `per` distinct steps (own query each)
+        cap_stream = torch.cuda.Stream()
+        per = max(d for d in range(1, 17) if args.steps % d == 0 and d <= n_q)
+        reps = args.steps // per
+        t_step, wall = timed_graph(full_step, reps, per)
+        mi, _ = timed_graph(index_only, max(1, reps), per)
+        ma, _ = timed_graph(attend_only, max(1, reps), per)
+        timing = f"HIP graph replay ({per} distinct steps per graph, {reps} replays)"
+        t_step_gpu = t_step
+    else:
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+        t0 = time.perf_counter()
+        for s in range(args.steps):
+            run_step(args.warmup + s, evs[s])
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        mi = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]) * 1e-3)
+        ma = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]) * 1e-3)
+        t_step_gpu = evs[0][0].elapsed_time(evs[-1][2]) * 1e-3 / args.steps if args.steps > 1 else wall
+        timing = "eager launches, events around each call"
     ms_per_step = wall / args.steps * 1e3
 
     # dense decode of the same layer
     dense_s = None
     if not args.no_dense:
-        for s in range(min(args.warmup, 5)):
-            kv, q, _ = step_args(s)
-            sdi.dense(kv, q, out=out, workspace=ws_dense, stream=stream)
+        for s in range(min(args.warmup, 3)):
+            dense_only(s)
         torch.cuda.synchronize()
-        dsteps = max(10, args.steps // 2)
-        dev_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(dsteps)]
-        for s in range(dsteps):
-            kv, q, _ = step_args(s)
-            dev_ev[s][0].record(stream)
-            sdi.dense(kv, q, out=out, workspace=ws_dense, stream=stream)
-            dev_ev[s][1].record(stream)
-        torch.cuda.synchronize()
-        dense_s = float(np.mean([e[0].elapsed_time(e[1]) for e in dev_ev]) * 1e-3)
+        if args.mode == "graph":
+            dense_s, _ = timed_graph(dense_only, max(1, reps // 2), per)
+        else:
+            dsteps = max(10, args.steps // 2)
+            dev_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(dsteps)]
+            for s in range(dsteps):
+                dev_ev[s][0].record(stream)
+                dense_only(s)
+                dev_ev[s][1].record(stream)
+            torch.cuda.synchronize()
+            dense_s = float(np.mean([e[0].elapsed_time(e[1]) for e in dev_ev]) * 1e-3)
 
     cold = {}
     if args.cold:
@@ -218,7 +276,6 @@ def main():
 
     kps0 = wl.k_per_seq()
     b_index, b_attend, b_dense = algorithmic_bytes(wl.seq_lens, kps0, B, hq, hkv)
-    mi, ma = float(t_index.mean()), float(t_attend.mean())
     step_bytes = b_index + b_attend
     value = args.steps / wall
     traffic = read_traffic()
@@ -239,7 +296,7 @@ def main():
                    "context_max": int(wl.n_max), "k_max": k_max, "sparsity": args.ratio,
                    "layout": wl.meta.get("layout"), "parallelism": "single GPU"},
         "step_GBps": step_bytes / (mi + ma) / 1e9, "step_pct_of_peak": 100 * step_bytes / (mi + ma) / PEAK_HBM_BPS,
-        "index_us": mi * 1e6, "attend_us": ma * 1e6, "gpu_step_us": t_step_gpu * 1e6,
+        "index_us": mi * 1e6, "attend_us": ma * 1e6, "gpu_step_us": t_step_gpu * 1e6, "timing": timing,
         "roofline": roofline, "roofline_attend": roofline_attend,
     }
     if dense_s is not None:

@@ -5,136 +5,312 @@
 // (sequence, query head) keep the k tokens with the largest raw score q . K_j,
 // lower index first on equal scores, per query head (paper section 1).
 //
-// Three launches on the caller's stream:
-//  1. zero_u32_kernel   clears the per-(b, h) first-digit histograms.
-//  2. score_kernel      streams every K page once per (b, kv head) and scores it
-//                       against the whole GQA group with one bf16 MFMA
-//                       (16x16x32: 16 head rows x 16 tokens per page), writes
-//                       order-preserving uint32 keys and counts the top 12 key
-//                       bits into an LDS histogram flushed with integer atomics.
-//  3. select_kernel     per (b, h): finds the threshold key from the histogram
-//                       plus two 10-bit radix passes over the keys, then writes
-//                       the selected indices in ascending order with one ordered
-//                       compaction pass (no sort needed).
+// Scores are fp32 sums of bf16 products from one MFMA instruction sequence; a
+// score's order-preserving uint32 key is its rank key.  Three launches:
+//
+//  1. zero_hist_kernel  clears the per-(b, h) 4096-bin histograms.
+//  2. score_kernel   streams every K page once per (b, kv head) with contiguous
+//                    non-temporal 1 KiB loads, transposes each page through LDS
+//                    into the MFMA operand layout, scores 16 tokens x up to 8
+//                    heads of the GQA group per 4 MFMAs (16x16x32 bf16), and
+//                    writes only the top 16 bits of each key ("code").  Codes are
+//                    staged in LDS and written as whole lines: interleaving key
+//                    writes with the K stream is what costs bandwidth, and 16-bit
+//                    codes halve it.  The top 12 code bits are counted into an LDS
+//                    histogram per head, flushed with integer atomics.
+//  3. select_kernel  per (b, h): the 12-bit histogram plus a 4-bit histogram of the
+//                    codes in the threshold bin give the code c* holding the k-th
+//                    key; one ordered-compaction pass
+//                    lists the tokens above c* (all selected) and the tokens with
+//                    code c*; the exact keys of the latter are recomputed with the
+//                    same MFMA sequence (bit-identical), an 8+8-bit radix on their
+//                    low halves gives the exact threshold, and the two ascending
+//                    lists are merged into the output.  If either list outgrows
+//                    LDS, the head is re-scored to full 32-bit keys in the
+//                    workspace and a generic radix select runs over them.
 #include "sdi_device.hpp"
 #include "sdi_launch.hpp"
 
 namespace sdi {
 
-constexpr int kScoreWaves = 4;
-constexpr int kScorePagesPerWave = 16;
-constexpr int kScoreUnroll = 4;
-constexpr int kScoreTokensPerBlock = kScoreWaves * kScorePagesPerWave * kPage;   // 1024
+// ---- score pass --------------------------------------------------------------------------
+constexpr int kScoreWaves = 8;
+constexpr int kScorePagesPerWave = 32;
+constexpr int kScoreUnroll = 2;                               // pages per register buffer
+constexpr int kHeadBlock = 8;                                 // query heads scored per workgroup
+constexpr int kScoreTokensPerBlock = kScoreWaves * kScorePagesPerWave * kPage;   // 4096
+constexpr int kStageRow = kRowBytes + 16;                     // padded LDS row: conflict-free both ways
+constexpr int kStagePage = kPage * kStageRow;                 // 4352 B
+constexpr int kCodeBlockPages = 8;                            // codes leave LDS every 8 pages (128 tokens)
+constexpr int kCodeBlock = kCodeBlockPages * kPage;
+static_assert(kScorePagesPerWave % kCodeBlockPages == 0, "code blocks tile a wave's pages");
+constexpr int kHistWordsPerHead = kHistBins / 2;              // two 16-bit counters per word
 
-constexpr int kSelThreads = 256;
-constexpr int kSelPerThread = 8;
-constexpr int kSelTile = kSelThreads * kSelPerThread;                           // 2048
-
-__global__ void zero_u32_kernel(uint32_t *__restrict__ p, int64_t n)
+__global__ void zero_hist_kernel(uint32_t *__restrict__ p, int64_t n)
 {
     int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
-    int64_t step = (int64_t)gridDim.x * blockDim.x * 4;
+    const int64_t step = (int64_t)gridDim.x * blockDim.x * 4;
     for (; i + 4 <= n; i += step) *(u32x4 *)(p + i) = u32x4{0u, 0u, 0u, 0u};
     for (; i < n; ++i) p[i] = 0u;
 }
 
-// grid (chunks of 1024 tokens, kv_heads * head_blocks, batch); 256 threads.
-// Dynamic LDS: min(16, group) * 2048 words (two 16-bit bin counters per word).
+// ---- select ------------------------------------------------------------------------------
+constexpr int kSelThreads = 1024;
+constexpr int kSelWaves = kSelThreads / 64;
+constexpr int kSelCodesPerThread = 32;                        // 64 B of codes per thread per round
+constexpr int kSelRound = kSelThreads * kSelCodesPerThread;   // 32768 tokens
+constexpr int kSelACap = 8192;                                // tokens above the threshold code
+constexpr int kSelCCap = 2048;                                // tokens sharing the threshold code
+constexpr int kSelPerThread = 8;                              // generic path
+constexpr int kSelTile = kSelThreads * kSelPerThread;
+
+__device__ __forceinline__ uint32_t code_at(const u32x4 (&w)[4], int e)
+{
+    const uint32_t word = w[e >> 3][(e >> 1) & 3];
+    return (e & 1) ? (word >> 16) : (word & 0xFFFFu);
+}
+
+// MFMA B operand for the q rows of a head block: lane (col, quad) holds head col's
+// dims 32 s + 8 quad .. +7 (zeros for heads past the block).
+__device__ __forceinline__ void load_q_operand(bf16x8 (&qb)[4], const uint16_t *__restrict__ q, int64_t row0,
+                                               int heads_here, int col, int quad)
+{
+    const bool live = col < heads_here;
+    const bf16x8 *qrow = (const bf16x8 *)(q + (row0 + (live ? col : 0)) * kHeadDim);
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+        qb[s] = live ? qrow[4 * s + quad] : __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+}
+
+// The score MFMA sequence: D[token 4 quad + i][head col] for 16 tokens (A: row col,
+// dims 32 s + 8 quad) and up to 16 heads (B).  Every recomputation uses this same
+// function so that keys agree bit for bit.
+__device__ __forceinline__ f32x4 score_mfma(const bf16x8 (&ka)[4], const bf16x8 (&qb)[4])
+{
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[s], qb[s], acc, 0, 0, 0);
+    return acc;
+}
+
+// grid (ceil(n_max / 4096), kv_heads * head_blocks, batch); 512 threads.
 __global__ __launch_bounds__(kScoreWaves * 64) void score_kernel(
     const uint16_t *__restrict__ kc, const int32_t *__restrict__ page_table,
     const int32_t *__restrict__ seq_lens, const uint16_t *__restrict__ q, int num_q_heads, int num_kv_heads,
-    int group, int head_blocks, int max_pages, uint32_t *__restrict__ keys, int64_t key_stride,
+    int group, int head_blocks, int max_pages, uint16_t *__restrict__ codes, int64_t code_stride,
     uint32_t *__restrict__ ghist)
 {
-    extern __shared__ uint32_t hist_lds[];
+    __shared__ int32_t pt_lds[kScoreWaves * kScorePagesPerWave];
+    __shared__ __attribute__((aligned(16))) unsigned char stage_all[kScoreWaves * kScoreUnroll * kStagePage];
+    __shared__ __attribute__((aligned(16))) uint16_t code_all[kScoreWaves * kHeadBlock * kCodeBlock];
+    __shared__ uint32_t hist_lds[kHeadBlock * kHistWordsPerHead];
     const int b = blockIdx.z;
     const int g = blockIdx.y / head_blocks, hb = blockIdx.y - g * head_blocks;
     const int n = seq_lens[b];
     const int tok0 = blockIdx.x * kScoreTokensPerBlock;
-    if (tok0 >= n) return;                                   // whole block exits together
-    const int heads_here = min(16, group - hb * 16);
-    const int h0 = g * group + hb * 16;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (tok0 >= n) return;                                    // whole block exits together
+    const int heads_here = min(kHeadBlock, group - hb * kHeadBlock);
+    const int h0 = g * group + hb * kHeadBlock;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int col = lane & 15, quad = lane >> 4;
-    const int words = heads_here * (kHistBins / 2);
-    for (int i = threadIdx.x; i < words; i += blockDim.x) hist_lds[i] = 0u;
+    unsigned char *stage = stage_all + wave * kScoreUnroll * kStagePage;
+    uint16_t *cstage = code_all + wave * kHeadBlock * kCodeBlock;
+    for (int i = threadIdx.x; i < heads_here * kHistWordsPerHead; i += blockDim.x) hist_lds[i] = 0u;
 
-    // MFMA A operand: row = head (col), k = 32 s + 8 quad .. +7.
-    bf16x8 qa[4];
-    {
-        const bool live = col < heads_here;
-        const bf16x8 *qrow =
-            (const bf16x8 *)(q + ((int64_t)b * num_q_heads + h0 + (live ? col : 0)) * kHeadDim);
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-            qa[s] = live ? qrow[4 * s + quad] : __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
-    }
-    __syncthreads();
+    bf16x8 qb[4];
+    load_q_operand(qb, q, (int64_t)b * num_q_heads + h0, heads_here, col, quad);
 
     const int pages_seq = (n + kPage - 1) / kPage;
-    const int p_begin = tok0 / kPage + wave * kScorePagesPerWave;
+    const int p_base = tok0 / kPage;                          // first page of this workgroup
+    const int p_begin = p_base + wave * kScorePagesPerWave;
     const int p_end = min(p_begin + kScorePagesPerWave, pages_seq);
-    const int32_t *pt = page_table + (int64_t)b * max_pages;
-    uint32_t *keys_h = keys + ((int64_t)b * num_q_heads + h0) * key_stride;
-    // MFMA B operand: column = token (row col of the page), k = 32 s + 8 quad .. +7.
-    const int lane_off = col * kHeadDim + quad * 8;
+    {
+        const int32_t *pt = page_table + (int64_t)b * max_pages;
+        const int i = threadIdx.x;
+        if (i < kScoreWaves * kScorePagesPerWave && p_base + i < pages_seq) pt_lds[i] = pt[p_base + i];
+    }
+    __syncthreads();                                          // page slice staged, histogram cleared
 
-    for (int p = p_begin; p < p_end; p += kScoreUnroll) {
-        bf16x8 kb[kScoreUnroll][4];
+    const uint16_t *k_head = kc + (int64_t)g * kPage * kHeadDim;                 // + phys * Hkv * 4 KiB
+    const int64_t page_elems = (int64_t)num_kv_heads * kPage * kHeadDim;
+    uint16_t *code_h = codes + ((int64_t)b * num_q_heads + h0) * code_stride;
+    // contiguous loads: chunk s (1 KiB) of a page, lane -> row 4 s + lane / 16, dims 8 (lane % 16)
+    const int wr_off = (lane >> 4) * kStageRow + (lane & 15) * 16;
+    // MFMA A operand: row col, dims 32 s + 8 quad -> bytes 64 s + 16 quad
+    const int rd_off = col * kStageRow + quad * 16;
+
+    auto load_group = [&](u32x4 (&kr)[kScoreUnroll][4], int p) {
+        int64_t phys[kScoreUnroll];
+#pragma unroll
+        for (int u = 0; u < kScoreUnroll; ++u) phys[u] = pt_lds[min(p + u, p_end - 1) - p_base];
 #pragma unroll
         for (int u = 0; u < kScoreUnroll; ++u) {
-            if (p + u < p_end) {
-                const int64_t phys = pt[p + u];
-                const bf16x8 *src =
-                    (const bf16x8 *)(kc + (phys * num_kv_heads + g) * (kPage * kHeadDim) + lane_off);
+            const u32x4 *src = (const u32x4 *)(k_head + phys[u] * page_elems) + lane;
 #pragma unroll
-                for (int s = 0; s < 4; ++s) kb[u][s] = src[4 * s];
-            }
+            for (int s = 0; s < 4; ++s) kr[u][s] = __builtin_nontemporal_load(src + 64 * s);
         }
+    };
+    auto score_group = [&](const u32x4 (&kr)[kScoreUnroll][4], int p) {
+#pragma unroll
+        for (int u = 0; u < kScoreUnroll; ++u)
+#pragma unroll
+            for (int s = 0; s < 4; ++s) *(u32x4 *)(stage + u * kStagePage + s * 4 * kStageRow + wr_off) = kr[u][s];
 #pragma unroll
         for (int u = 0; u < kScoreUnroll; ++u) {
-            if (p + u < p_end) {
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            const int pp = p + u;
+            if (pp < p_end) {                                 // wave-uniform
+                bf16x8 ka[4];
 #pragma unroll
-                for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[s], kb[u][s], acc, 0, 0, 0);
-                const int t = (p + u) * kPage + col;
-                if (t < n) {
+                for (int s = 0; s < 4; ++s) ka[s] = *(const bf16x8 *)(stage + u * kStagePage + s * 64 + rd_off);
+                const f32x4 acc = score_mfma(ka, qb);
+                // lane holds tokens 4 quad .. +3 of head col: stage their codes
+                const uint32_t c0 = score_key(acc[0]) >> 16, c1 = score_key(acc[1]) >> 16;
+                const uint32_t c2 = score_key(acc[2]) >> 16, c3 = score_key(acc[3]) >> 16;
+                const int slot = (pp - p_begin) & (kCodeBlockPages - 1);
+                if (col < heads_here) {
+                    *(uint2 *)(cstage + col * kCodeBlock + slot * kPage + 4 * quad) =
+                        uint2{c0 | (c1 << 16), c2 | (c3 << 16)};
+                    const int t0 = pp * kPage + 4 * quad;
+                    uint32_t *hrow = hist_lds + col * kHistWordsPerHead;
+                    const uint32_t cs[4] = {c0, c1, c2, c3};
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const int hm = quad * 4 + i;
-                        if (hm < heads_here) {
-                            const uint32_t key = score_key(acc[i]);
-                            keys_h[hm * key_stride + t] = key;
-                            const uint32_t bin = key >> kHistShift;
-                            atomicAdd(&hist_lds[hm * (kHistBins / 2) + (bin >> 1)], 1u << ((bin & 1u) * 16u));
+                        const uint32_t bin = cs[i] >> 4;             // top 12 key bits
+                        if (t0 + i < n) atomicAdd(&hrow[bin >> 1], 1u << ((bin & 1u) * 16u));
+                    }
+                }
+                if (slot == kCodeBlockPages - 1 || pp == p_end - 1) {
+                    // flush: lane -> head (lane / 16) + 4 j, 8 tokens (16 B) at 8 (lane % 16)
+                    const int tb = (pp - slot) * kPage;
+                    const int tt = 8 * (lane & 15);
+                    for (int hh = lane >> 4; hh < heads_here; hh += 4) {
+                        const u32x4 v = *(const u32x4 *)(cstage + hh * kCodeBlock + tt);
+                        uint16_t *dst = code_h + hh * code_stride + tb + tt;
+                        if (tb + tt + 8 <= n) {
+                            *(u32x4 *)dst = v;
+                        } else {
+                            for (int e = 0; e < 8; ++e)
+                                if (tb + tt + e < n) dst[e] = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
                         }
                     }
                 }
             }
         }
+    };
+
+    if (p_begin < p_end) {                                    // wave-uniform
+        u32x4 ka[kScoreUnroll][4], kb[kScoreUnroll][4];
+        load_group(ka, p_begin);
+        for (int p = p_begin; p < p_end; p += 2 * kScoreUnroll) {
+            load_group(kb, p + kScoreUnroll);
+            score_group(ka, p);
+            load_group(ka, p + 2 * kScoreUnroll);
+            score_group(kb, p + kScoreUnroll);
+        }
     }
     __syncthreads();
     uint32_t *gh = ghist + ((int64_t)b * num_q_heads + h0) * kHistBins;
-    for (int i = threadIdx.x; i < words; i += blockDim.x) {
-        const uint32_t w = hist_lds[i];
-        if (w) {
-            const int hm = i / (kHistBins / 2);
-            const int bin = (i - hm * (kHistBins / 2)) * 2;
-            uint32_t *dst = gh + hm * kHistBins + bin;
-            if (w & 0xFFFFu) atomicAdd(dst, w & 0xFFFFu);
-            if (w >> 16) atomicAdd(dst + 1, w >> 16);
+    for (int i = threadIdx.x; i < heads_here * kHistWordsPerHead; i += blockDim.x) {
+        const uint32_t wv = hist_lds[i];
+        if (wv) {
+            const int hm = i / kHistWordsPerHead;
+            uint32_t *dst = gh + hm * kHistBins + (i - hm * kHistWordsPerHead) * 2;
+            if (wv & 0xFFFFu) atomicAdd(dst, wv & 0xFFFFu);
+            if (wv >> 16) atomicAdd(dst + 1, wv >> 16);
         }
     }
 }
 
-// Keys [start, start + 8) clipped to n; returns how many are valid.
-__device__ __forceinline__ int load_keys8(const uint32_t *__restrict__ src, int start, int n, uint32_t *v)
+// ---- select helpers ----------------------------------------------------------------------
+
+// Largest bin B of hist[0..nbins) (nbins = 64 * per, per <= 64) with
+// sum_{bins >= B} >= need, found by one wave in two parallel levels: lane l sums
+// bins top - l*per ... (from the highest bins down), a wave scan locates the lane
+// group holding the crossing, and a second scan over that group's `per` bins
+// locates the bin.  Every lane of the calling wave gets bin and above (the count
+// over bins > B).  Returns false (outputs untouched) if the total is below need.
+__device__ __forceinline__ bool wave_threshold(const uint32_t *hist, int nbins, uint32_t need, uint32_t &bin,
+                                               uint32_t &above)
+{
+    const int lane = threadIdx.x & 63, per = nbins / 64;
+    const int top = nbins - 1 - lane * per;
+    uint32_t mine = 0;
+    for (int i = 0; i < per; ++i) mine += hist[top - i];
+    const uint32_t x = wave_inclusive_scan(mine);
+    const uint64_t cross = __ballot(x >= need);
+    if (cross == 0) return false;
+    const int L = __ffsll((unsigned long long)cross) - 1;
+    const uint32_t before = __shfl(x - mine, L, 64);
+    const int top_l = nbins - 1 - L * per;
+    const uint32_t c = lane < per ? hist[top_l - lane] : 0u;
+    const uint32_t y = before + wave_inclusive_scan(c);
+    const uint64_t cross2 = __ballot(lane < per && y >= need);
+    const int I = __ffsll((unsigned long long)cross2) - 1;
+    bin = (uint32_t)(top_l - I);
+    above = __shfl(y - c, I, 64);
+    return true;
+}
+
+// Workgroup form: wave 0 searches, res[0] = bin, res[1] = above; ends with a barrier.
+__device__ __forceinline__ void threshold_bin_wave(const uint32_t *hist, int nbins, uint32_t need, uint32_t *res)
+{
+    if (threadIdx.x < 64) {
+        uint32_t bin, above;
+        if (wave_threshold(hist, nbins, need, bin, above) && threadIdx.x == 0) { res[0] = bin; res[1] = above; }
+    }
+    __syncthreads();
+}
+
+__device__ __forceinline__ void wave_lds_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Number of entries of the ascending list a[0..len) that are < x.
+__device__ __forceinline__ int count_below(const uint32_t *a, int len, uint32_t x)
+{
+    int lo = 0, hi = len;
+    while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (a[mid] < x) lo = mid + 1; else hi = mid;
+    }
+    return lo;
+}
+
+// Codes [start, start + 32) of a row into four 16-byte words (zeros past n).
+__device__ __forceinline__ int load_codes(const uint16_t *__restrict__ row, int start, int n, u32x4 (&w)[4])
+{
+    if (start + kSelCodesPerThread <= n) {
+        const u32x4 *src = (const u32x4 *)(row + start);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[i] = src[i];
+        return kSelCodesPerThread;
+    }
+    const int cnt = n > start ? n - start : 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        uint32_t x[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int e0 = 8 * i + 2 * j;
+            const uint32_t lo = e0 < cnt ? row[start + e0] : 0u;
+            const uint32_t hi = e0 + 1 < cnt ? row[start + e0 + 1] : 0u;
+            x[j] = lo | (hi << 16);
+        }
+        w[i] = u32x4{x[0], x[1], x[2], x[3]};
+    }
+    return cnt;
+}
+
+// Keys [start, start + 8) of a 32-bit key row, clipped to n.
+__device__ __forceinline__ int load_keys8(const uint32_t *__restrict__ src, int start, int n, uint32_t (&v)[8])
 {
     if (start + 8 <= n) {
-        const u32x4 a = *(const u32x4 *)(src + start);
-        const u32x4 c = *(const u32x4 *)(src + start + 4);
-        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-        v[4] = c.x; v[5] = c.y; v[6] = c.z; v[7] = c.w;
+        const u32x4 a = *(const u32x4 *)(src + start), c = *(const u32x4 *)(src + start + 4);
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = c.x; v[5] = c.y; v[6] = c.z; v[7] = c.w;
         return 8;
     }
     const int cnt = n > start ? n - start : 0;
@@ -143,57 +319,49 @@ __device__ __forceinline__ int load_keys8(const uint32_t *__restrict__ src, int 
     return cnt;
 }
 
-// grid (num_q_heads, batch); 256 threads.
-__global__ __launch_bounds__(kSelThreads) void select_kernel(
-    const uint32_t *__restrict__ keys, int64_t key_stride, const uint32_t *__restrict__ ghist,
-    const int32_t *__restrict__ seq_lens, const int32_t *__restrict__ k_per_seq, int num_q_heads, int k_max,
-    int32_t *__restrict__ idx_out)
+// Exact 32-bit keys of up to 16 tokens of one head block: the 16 K rows (cache row
+// number per lane `col`, or -1) as the MFMA A operand, the block's q as B.  Lanes
+// with col == head-in-block return the scores of tokens 4 quad .. +3.
+__device__ __forceinline__ f32x4 rescore16(const uint16_t *__restrict__ kc, int row, const bf16x8 (&qb)[4],
+                                          int quad)
 {
-    __shared__ uint32_t hist[kHistBins];
-    __shared__ uint32_t scratch[kSelThreads / 64 + 2];
-    const int h = blockIdx.x, b = blockIdx.y;
-    const int64_t bh = (int64_t)b * num_q_heads + h;
-    const int n = seq_lens[b];
-    int kk = min(min(k_per_seq[b], n), k_max);
-    if (kk < 0) kk = 0;
-    int32_t *out = idx_out + bh * k_max;
-    if (kk == n || kk == 0) {                                // everything, or nothing
-        for (int i = threadIdx.x; i < k_max; i += kSelThreads) out[i] = i < kk ? i : -1;
-        return;
-    }
-    const uint32_t *kh = keys + bh * key_stride;
+    bf16x8 ka[4];
+    const bf16x8 *src = (const bf16x8 *)(kc + (int64_t)(row < 0 ? 0 : row) * kHeadDim);
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+        ka[s] = row >= 0 ? src[4 * s + quad] : __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+    return score_mfma(ka, qb);
+}
 
-    // Digit 1 (top 12 bits) was counted by the score pass.
-    for (int i = threadIdx.x; i < kHistBins; i += kSelThreads) hist[i] = ghist[bh * kHistBins + i];
-    if (threadIdx.x == 0) { scratch[kSelThreads / 64] = 0u; scratch[kSelThreads / 64 + 1] = 0u; }
-    __syncthreads();
-    uint32_t above;
-    uint32_t prefix = (uint32_t)threshold_bin<kSelThreads>(hist, kHistBins, (uint32_t)kk, scratch, above);
-    uint32_t need = (uint32_t)kk - above;                    // >= 1 keys still to take inside the bin
-
-    // Digits 2 and 3 (10 bits each) among the keys that share the prefix.
-    int shift = kHistShift;
+// Generic select over full 32-bit keys in memory: 12 + 10 + 10-bit radix passes,
+// then one ordered-compaction pass writes the selection.
+__device__ void select_generic(const uint32_t *__restrict__ kh, int n, int kk, int k_max, uint32_t *hist,
+                               uint32_t *scratch, uint32_t *res, int32_t *__restrict__ out)
+{
+    uint32_t prefix = 0, need = (uint32_t)kk;
+    int shift = 32;
 #pragma unroll 1
-    for (int pass = 0; pass < 2; ++pass) {
-        const int lo = shift - 10;
-        for (int i = threadIdx.x; i < 1024; i += kSelThreads) hist[i] = 0u;
+    for (int pass = 0; pass < 3; ++pass) {
+        const int w = pass == 0 ? 12 : 10, lo = shift - w, nb = 1 << w;
+        for (int i = threadIdx.x; i < nb; i += kSelThreads) hist[i] = 0u;
+        if (threadIdx.x == 0) { res[0] = 0u; res[1] = 0u; }
         __syncthreads();
         for (int base = 0; base < n; base += kSelTile) {
             uint32_t v[8];
             const int cnt = load_keys8(kh, base + threadIdx.x * kSelPerThread, n, v);
 #pragma unroll
             for (int e = 0; e < 8; ++e)
-                if (e < cnt && (v[e] >> shift) == prefix) atomicAdd(&hist[(v[e] >> lo) & 1023u], 1u);
+                if (e < cnt && (shift == 32 || (v[e] >> shift) == prefix))
+                    atomicAdd(&hist[(v[e] >> lo) & (uint32_t)(nb - 1)], 1u);
         }
         __syncthreads();
-        const uint32_t d = (uint32_t)threshold_bin<kSelThreads>(hist, 1024, need, scratch, above);
-        need -= above;
-        prefix = (prefix << 10) | d;
+        threshold_bin_wave(hist, nb, need, res);
+        need -= res[1];
+        prefix = (shift == 32 ? 0u : (prefix << w)) | res[0];
         shift = lo;
+        __syncthreads();                                     // res consumed before its next write
     }
-
-    // Threshold key T and r = how many keys equal to T to take (lowest indices first).
-    const uint32_t T = prefix, r = need;
+    const uint32_t T = prefix, r = need;                     // take keys > T and the first r keys == T
     uint32_t run_sel = 0, run_eq = 0;
     for (int base = 0; base < n; base += kSelTile) {
         uint32_t v[8];
@@ -216,7 +384,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
                 bool take = v[e] > T;
                 if (v[e] == T) take = (eq_rank++ < r);
                 if (take) {
-                    if (pos < (uint32_t)kk) out[pos] = start + e;   // never past this row
+                    if (pos < (uint32_t)kk) out[pos] = start + e;
                     ++pos;
                 }
             }
@@ -227,40 +395,238 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     for (int i = (int)run_sel + threadIdx.x; i < k_max; i += kSelThreads) out[i] = -1;
 }
 
-size_t index_topk_key_stride(int n_max) { return (size_t)((n_max + 63) / 64) * 64; }
+struct SelectArgs {
+    const uint16_t *kc;
+    const int32_t *page_table, *seq_lens, *k_per_seq;
+    const uint16_t *q;
+    const uint16_t *codes;
+    const uint32_t *ghist;                                    // 4096-bin histogram of the top 12 code bits
+    uint32_t *keys32;                                         // generic-path scratch, one row per (b, h)
+    int64_t stride;
+    int num_q_heads, num_kv_heads, group, max_pages, k_max;
+    int32_t *idx_out;
+};
+
+// grid (num_q_heads, batch); 1024 threads.
+__global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a)
+{
+    __shared__ uint32_t whist[kSelWaves * 256];               // digit 1 per wave; later other histograms
+    __shared__ uint32_t hist2[256];
+    __shared__ uint32_t A[kSelACap];                          // tokens above the threshold code
+    __shared__ uint32_t Ci[kSelCCap];                         // tokens with the threshold code
+    __shared__ uint32_t Ck[kSelCCap];                         // their exact keys
+    __shared__ uint32_t scratch[kSelWaves + 2];
+    __shared__ uint32_t res[8];
+    const int h = blockIdx.x, b = blockIdx.y;
+    const int64_t bh = (int64_t)b * a.num_q_heads + h;
+    const int n = a.seq_lens[b];
+    int kk = min(min(a.k_per_seq[b], n), a.k_max);
+    if (kk < 0) kk = 0;
+    int32_t *out = a.idx_out + bh * a.k_max;
+    if (kk == n || kk == 0) {                                 // everything, or nothing
+        for (int i = threadIdx.x; i < a.k_max; i += kSelThreads) out[i] = i < kk ? i : -1;
+        return;
+    }
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int col = lane & 15, quad = lane >> 4;
+    const int g = h / a.group, hl = h - g * a.group, hb = hl / kHeadBlock, hn = hl - hb * kHeadBlock;
+    const int heads_here = min(kHeadBlock, a.group - hb * kHeadBlock);
+    const int64_t q_row0 = (int64_t)b * a.num_q_heads + g * a.group + hb * kHeadBlock;
+    const int32_t *pt = a.page_table + (int64_t)b * a.max_pages;
+    const uint16_t *crow = a.codes + bh * a.stride;
+    const int rounds = (n + kSelRound - 1) / kSelRound;
+
+    u32x4 w[4];
+    int cnt = load_codes(crow, threadIdx.x * kSelCodesPerThread, n, w);
+    for (int i = threadIdx.x; i < kHistBins; i += kSelThreads) whist[i] = a.ghist[bh * kHistBins + i];
+    if (threadIdx.x < 256) hist2[threadIdx.x] = 0u;
+    if (threadIdx.x < 8) res[threadIdx.x] = 0u;
+    __syncthreads();
+    // digit 1 (code bits 15..4) was counted by the score pass
+    threshold_bin_wave(whist, kHistBins, (uint32_t)kk, res);
+    const uint32_t d1 = res[0], above1 = res[1];
+    // digit 2 (code bits 3..0) among codes whose digit 1 is d1
+    for (int r = 0; r < rounds; ++r) {
+        if (rounds > 1) cnt = load_codes(crow, r * kSelRound + threadIdx.x * kSelCodesPerThread, n, w);
+#pragma unroll
+        for (int e = 0; e < kSelCodesPerThread; ++e) {
+            const uint32_t c = code_at(w, e);
+            if (e < cnt && (c >> 4) == d1) atomicAdd(&hist2[c & 15u], 1u);
+        }
+    }
+    __syncthreads();
+    threshold_bin_wave(hist2, 64, (uint32_t)kk - above1, res + 2);   // bins 16..63 are empty
+    const uint32_t cstar = (d1 << 4) | res[2];
+    const uint32_t above = above1 + res[3];
+    const uint32_t in_bin = hist2[res[2]];
+    uint32_t need = (uint32_t)kk - above;                     // >= 1 of the in_bin tokens
+
+    if (above > (uint32_t)kSelACap || in_bin > (uint32_t)kSelCCap) {
+        // Generic path: re-score this head to full keys, then radix-select over them.
+        uint32_t *krow = a.keys32 + bh * a.stride;
+        bf16x8 qb[4];
+        load_q_operand(qb, a.q, q_row0, heads_here, col, quad);
+        for (int t0 = wave * 16; t0 < n; t0 += kSelWaves * 16) {
+            const int tok = t0 + col;
+            const int row = tok < n ? (pt[tok >> 4] * a.num_kv_heads + g) * kPage + (tok & 15) : -1;
+            const f32x4 acc = rescore16(a.kc, row, qb, quad);
+            if (col == hn) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (t0 + 4 * quad + i < n) krow[t0 + 4 * quad + i] = score_key(acc[i]);
+            }
+        }
+        __threadfence_block();
+        __syncthreads();
+        select_generic(krow, n, kk, a.k_max, whist, scratch, res, out);
+        return;
+    }
+
+    // ordered compaction: A = tokens with code > c*, C = tokens with code == c*
+    uint32_t run_a = 0, run_c = 0;
+    for (int r = 0; r < rounds; ++r) {
+        const int start = r * kSelRound + threadIdx.x * kSelCodesPerThread;
+        if (rounds > 1) cnt = load_codes(crow, start, n, w);
+        uint32_t ma = 0, mc = 0;
+#pragma unroll
+        for (int e = 0; e < kSelCodesPerThread; ++e) {
+            const uint32_t c = code_at(w, e);
+            ma |= (e < cnt && c > cstar) ? (1u << e) : 0u;
+            mc |= (e < cnt && c == cstar) ? (1u << e) : 0u;
+        }
+        uint32_t tot;
+        const uint32_t pre = block_exclusive_scan<kSelThreads>(((uint32_t)__popc(mc) << 16) | (uint32_t)__popc(ma),
+                                                               scratch, tot);
+        uint32_t pa = run_a + (pre & 0xFFFFu), pc = run_c + (pre >> 16);
+        while (ma) {
+            const int e = __builtin_ctz(ma);
+            ma &= ma - 1u;
+            if (pa < (uint32_t)kSelACap) A[pa] = (uint32_t)(start + e);
+            ++pa;
+        }
+        while (mc) {
+            const int e = __builtin_ctz(mc);
+            mc &= mc - 1u;
+            if (pc < (uint32_t)kSelCCap) Ci[pc] = (uint32_t)(start + e);
+            ++pc;
+        }
+        run_a += tot & 0xFFFFu;
+        run_c += tot >> 16;
+    }
+    __syncthreads();
+    const int na_tot = (int)min(run_a, (uint32_t)kSelACap);
+    const int m = (int)min(run_c, (uint32_t)kSelCCap);
+
+    // exact keys of C: 16 candidates per MFMA group, one group per wave at a time
+    {
+        bf16x8 qb[4];
+        load_q_operand(qb, a.q, q_row0, heads_here, col, quad);
+        for (int c0 = wave * 16; c0 < m; c0 += kSelWaves * 16) {
+            int row = -1;
+            if (c0 + col < m) {
+                const int tok = (int)Ci[c0 + col];
+                row = (pt[tok >> 4] * a.num_kv_heads + g) * kPage + (tok & 15);
+            }
+            const f32x4 acc = rescore16(a.kc, row, qb, quad);
+            if (col == hn) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (c0 + 4 * quad + i < m) Ck[c0 + 4 * quad + i] = score_key(acc[i]);
+            }
+        }
+    }
+    if (threadIdx.x < 256) { whist[threadIdx.x] = 0u; hist2[threadIdx.x] = 0u; }
+    __syncthreads();
+
+    // Exact threshold inside C and the selected candidates, by wave 0 alone:
+    // key bits 15..8, then 7..0 (bits 31..16 are c*); then keep key > T, or key == T
+    // among the first r, in token order, into Cs.
+    uint32_t *Cs = whist + 1024;                              // up to kSelCCap selected candidates
+    if (threadIdx.x < 64) {
+        for (int i = lane; i < m; i += 64) atomicAdd(&whist[(Ck[i] >> 8) & 255u], 1u);
+        wave_lds_sync();
+        uint32_t d3 = 0, ab3 = 0;
+        wave_threshold(whist, 256, need, d3, ab3);
+        need -= ab3;
+        const uint32_t pref3 = (cstar << 8) | d3;
+        for (int i = lane; i < m; i += 64)
+            if ((Ck[i] >> 8) == pref3) atomicAdd(&hist2[Ck[i] & 255u], 1u);
+        wave_lds_sync();
+        uint32_t d4 = 0, ab4 = 0;
+        wave_threshold(hist2, 256, need, d4, ab4);
+        need -= ab4;
+        const uint32_t T = (pref3 << 8) | d4, r = need;
+        const int per = (m + 63) / 64;                        // entries owned by each lane, in order
+        uint32_t gt = 0, eq = 0;
+        for (int e = 0; e < per; ++e) {
+            const int i = lane * per + e;
+            if (i < m) { gt += Ck[i] > T ? 1u : 0u; eq += Ck[i] == T ? 1u : 0u; }
+        }
+        const uint32_t inc = wave_inclusive_scan((eq << 16) | gt);
+        const uint32_t pre = inc - ((eq << 16) | gt);
+        uint32_t pos = (pre & 0xFFFFu) + min(pre >> 16, r);
+        uint32_t eq_rank = pre >> 16;
+        for (int e = 0; e < per; ++e) {
+            const int i = lane * per + e;
+            if (i < m) {
+                const uint32_t k = Ck[i];
+                bool take = k > T;
+                if (k == T) take = (eq_rank++ < r);
+                if (take) Cs[pos++] = Ci[i];
+            }
+        }
+        const uint32_t all = __shfl(inc, 63, 64);
+        if (lane == 0) res[0] = min((all & 0xFFFFu) + min(all >> 16, r), (uint32_t)m);
+    }
+    __syncthreads();
+    const int ns = (int)res[0];                               // selected candidates
+
+    // merge the two ascending lists into the output row
+    for (int i = threadIdx.x; i < na_tot; i += kSelThreads) {
+        const uint32_t x = A[i];
+        out[i + count_below(Cs, ns, x)] = (int32_t)x;
+    }
+    for (int j = threadIdx.x; j < ns; j += kSelThreads) {
+        const uint32_t x = Cs[j];
+        out[j + count_below(A, na_tot, x)] = (int32_t)x;
+    }
+    for (int i = na_tot + ns + threadIdx.x; i < a.k_max; i += kSelThreads) out[i] = -1;
+}
+
+// ---- host side ---------------------------------------------------------------------------
+
+size_t index_topk_key_stride(int n_max) { return (size_t)((n_max + 127) / 128) * 128; }
 
 size_t index_topk_workspace_bytes(int batch, int num_q_heads, int n_max)
 {
-    const size_t bh = (size_t)batch * num_q_heads;
-    return bh * (index_topk_key_stride(n_max) + kHistBins) * sizeof(uint32_t);
+    // per (b, h): a 32-bit key row for the generic path, the 16-bit codes, the 4096-bin histogram
+    return (size_t)batch * num_q_heads *
+           (index_topk_key_stride(n_max) * (sizeof(uint32_t) + sizeof(uint16_t)) + kHistBins * sizeof(uint32_t));
 }
 
 hipError_t launch_index_topk(const IndexArgs &a, hipStream_t stream)
 {
     const int group = a.num_q_heads / a.num_kv_heads;
-    const int head_blocks = (group + 15) / 16;
-    const int64_t key_stride = (int64_t)index_topk_key_stride(a.n_max);
-    const int64_t bh = (int64_t)a.batch * a.num_q_heads;
-    uint32_t *keys = (uint32_t *)a.ws;
-    uint32_t *ghist = keys + bh * key_stride;
+    const int head_blocks = (group + kHeadBlock - 1) / kHeadBlock;
+    const int64_t stride = (int64_t)index_topk_key_stride(a.n_max);
+    const size_t rows = (size_t)a.batch * a.num_q_heads;
+    uint32_t *keys32 = (uint32_t *)a.ws;
+    uint32_t *ghist = keys32 + rows * stride;
+    uint16_t *codes = (uint16_t *)(ghist + rows * kHistBins);
 
-    const int64_t hist_words = bh * kHistBins;
-    const int zblocks = (int)std::min<int64_t>(2048, (hist_words / 4 + 255) / 256 + 1);
-    hipLaunchKernelGGL(zero_u32_kernel, dim3(zblocks), dim3(256), 0, stream, ghist, hist_words);
+    const int64_t hist_words = (int64_t)rows * kHistBins;
+    const int zblocks = (int)std::min<int64_t>(1024, (hist_words / 4 + 255) / 256);
+    hipLaunchKernelGGL(zero_hist_kernel, dim3(std::max(zblocks, 1)), dim3(256), 0, stream, ghist, hist_words);
 
-    const int heads_max = std::min(16, group);
-    const size_t lds = (size_t)heads_max * (kHistBins / 2) * sizeof(uint32_t);
-    if (lds > 64 * 1024) {
-        hipError_t e = hipFuncSetAttribute((const void *)score_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
-    }
     dim3 sgrid((a.n_max + kScoreTokensPerBlock - 1) / kScoreTokensPerBlock, a.num_kv_heads * head_blocks, a.batch);
-    hipLaunchKernelGGL(score_kernel, sgrid, dim3(kScoreWaves * 64), lds, stream, (const uint16_t *)a.k_cache,
+    hipLaunchKernelGGL(score_kernel, sgrid, dim3(kScoreWaves * 64), 0, stream, (const uint16_t *)a.k_cache,
                        a.page_table, a.seq_lens, (const uint16_t *)a.q, a.num_q_heads, a.num_kv_heads, group,
-                       head_blocks, a.max_pages, keys, key_stride, ghist);
+                       head_blocks, a.max_pages, codes, stride, ghist);
 
-    hipLaunchKernelGGL(select_kernel, dim3(a.num_q_heads, a.batch), dim3(kSelThreads), 0, stream, keys, key_stride,
-                       ghist, a.seq_lens, a.k_per_seq, a.num_q_heads, a.k_max, a.idx_out);
+    SelectArgs s{(const uint16_t *)a.k_cache, a.page_table, a.seq_lens, a.k_per_seq, (const uint16_t *)a.q,
+                 codes, ghist, keys32, stride, a.num_q_heads, a.num_kv_heads, group, a.max_pages, a.k_max,
+                 a.idx_out};
+    hipLaunchKernelGGL(select_kernel, dim3(a.num_q_heads, a.batch), dim3(kSelThreads), 0, stream, s);
     return hipGetLastError();
 }
 

@@ -11,9 +11,8 @@ namespace sdi {
 constexpr int kHeadDim = 128;
 constexpr int kPage = 16;
 constexpr int kRowBytes = kHeadDim * 2;        // one bf16 row
-constexpr int kHistBits = 12;                  // first radix digit (written by the score pass)
+constexpr int kHistBits = 12;                  // first radix digit of a key (counted by the score pass)
 constexpr int kHistBins = 1 << kHistBits;
-constexpr int kHistShift = 32 - kHistBits;
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
@@ -72,6 +71,20 @@ __device__ __forceinline__ float row16_max(float v)
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Inclusive prefix sum over the 64 lanes of a wave with DPP: row_shr 1/2/4/8 inside
+// each 16-lane row, then row_bcast 15 (into rows 1 and 3) and row_bcast 31 (into rows
+// 2 and 3).  Lanes whose DPP source does not exist receive 0.
+__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v)
+{
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, false);   // row_shr:1
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, false);   // row_shr:2
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, false);   // row_shr:4
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, false);   // row_shr:8
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false);   // row_bcast:15
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false);   // row_bcast:31
+    return v;
+}
+
 // Exclusive prefix sum over a workgroup of NT threads (NT a multiple of 64).
 // `scratch` needs NT/64 words of LDS.  Returns this thread's exclusive prefix and
 // sets `total`.  Contains two workgroup barriers.
@@ -79,12 +92,7 @@ template <int NT>
 __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t *scratch, uint32_t &total)
 {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    uint32_t x = v;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        uint32_t y = __shfl_up(x, o, 64);
-        if (lane >= o) x += y;
-    }
+    const uint32_t x = wave_inclusive_scan(v);
     if (lane == 63) scratch[wave] = x;
     __syncthreads();
     uint32_t before = 0, all = 0;
@@ -97,38 +105,6 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t *s
     __syncthreads();
     total = all;
     return before + x - v;
-}
-
-// Largest bin B of hist[0..nbins) (counts) with sum_{bins >= B} >= need (need >= 1,
-// and the total must reach it).  Returns B; `above` = sum over bins > B.
-// All NT threads must call it; `scratch` needs NT/64 + 2 words of LDS.
-template <int NT>
-__device__ __forceinline__ int threshold_bin(const uint32_t *hist, int nbins, uint32_t need, uint32_t *scratch,
-                                             uint32_t &above)
-{
-    const int per = nbins / NT;               // bins per thread, taken from the top down
-    const int top = nbins - 1 - threadIdx.x * per;
-    uint32_t mine = 0;
-    for (int i = 0; i < per; ++i) mine += hist[top - i];
-    uint32_t total;
-    uint32_t before = block_exclusive_scan<NT>(mine, scratch, total);
-    if (before < need && before + mine >= need) {
-        uint32_t run = before;
-        for (int i = 0; i < per; ++i) {
-            uint32_t c = hist[top - i];
-            if (run + c >= need) {
-                scratch[NT / 64] = (uint32_t)(top - i);
-                scratch[NT / 64 + 1] = run;
-                break;
-            }
-            run += c;
-        }
-    }
-    __syncthreads();
-    int bin = (int)scratch[NT / 64];
-    above = scratch[NT / 64 + 1];
-    __syncthreads();
-    return bin;
 }
 
 }  // namespace sdi

@@ -52,7 +52,7 @@ def test_strerror_covers_every_code(lib):
 def test_workspace_sizes(lib):
     k = kv()
     n1 = lib.sparse_decode_index_topk_workspace(ctypes.byref(k), 8, 5)
-    assert n1 == 2 * 8 * (192 + 4096) * 4                # keys padded to 64 + 4096-bin histogram
+    assert n1 == 2 * 8 * (256 * 6 + 4096 * 4)            # per row: 32-bit keys + 16-bit codes (padded to 128) + histogram
     assert lib.sparse_decode_attend_workspace(ctypes.byref(k), 8, 256) == 0          # one chunk: no partials
     assert lib.sparse_decode_attend_workspace(ctypes.byref(k), 8, 257) == 2 * 8 * 2 * 130 * 4
     assert lib.dense_decode_workspace(ctypes.byref(k), 8) == 2 * 8 * 2 * 130 * 4

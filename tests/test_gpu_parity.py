@@ -263,3 +263,62 @@ def test_full_size_sampled(cfg, sample):
     check_indices(gidx[sub], oidx, s, kth, cache.sl, kps[sub])
     check_close(out[sub], oracle.attend(cache, q, gidx[sub]), what=f"C{cfg} attend")
     check_close(dn[sub], oracle.dense(cache, q), what=f"C{cfg} dense")
+
+
+def test_select_fallback_paths():
+    """Threshold bins too large for the LDS candidate list (all keys tied; few distinct
+    integer scores over a long context) and an above-bin list larger than its LDS
+    capacity take the general multi-pass select; results must still be exact."""
+    rng = np.random.default_rng(11)
+    n = 12000
+    krow = bf16_round(rng.standard_normal(128))
+    k = [np.broadcast_to(krow, (1, n, 128)).copy()]
+    v = [bf16_round(rng.standard_normal((1, n, 128)))]
+    case = TinyCase(k, v, bf16_round(rng.standard_normal((1, 4, 128))))
+    dev = DeviceCase.of_tiny(case)
+    gidx = dev.index(np.array([700], np.int32), 700)
+    assert np.array_equal(gidx[0], np.broadcast_to(np.arange(700), (4, 700)))
+    case = random_case(rng, batch=2, hq=4, hkv=1, lens=[20000, 17000], integer=True, lo=-1, hi=1)
+    dev = DeviceCase.of_tiny(case)
+    cache = oracle.Cache(case.k_cache, case.v_cache, case.page_table, case.lens)
+    run_and_check(dev, cache, case.q, np.array([9000, 400], np.int32), 9000, strict=True, check_dense=False,
+                  tag="fallback")
+
+
+def test_graph_replay_matches_eager():
+    """A decode step (index -> attend) and dense decode captured in one HIP graph and
+    replayed several times, with eager work and synchronisation between replays:
+    every replay must reproduce the eager results bit for bit."""
+    wl = synth.config(2, n=5000, batch=2)
+    dev = DeviceCase.of_workload(wl)
+    kps = i32_tensor(wl.k_per_seq())
+    k_max = wl.k_max()
+    B, hq = wl.batch, wl.num_q_heads
+    idx = torch.empty((B, hq, k_max), dtype=torch.int32, device="cuda")
+    out = torch.empty((B, hq, 128), dtype=torch.float32, device="cuda")
+    dn = torch.empty_like(out)
+    ws_i = torch.empty(sdi.index_topk_workspace_bytes(dev.kv, hq, k_max), dtype=torch.uint8, device="cuda")
+    ws_a = torch.empty(max(1, sdi.attend_workspace_bytes(dev.kv, hq, k_max)), dtype=torch.uint8, device="cuda")
+    ws_d = torch.empty(sdi.dense_workspace_bytes(dev.kv, hq), dtype=torch.uint8, device="cuda")
+
+    def step():
+        st = torch.cuda.current_stream()
+        sdi.index_topk(dev.kv, dev.q, kps, k_max, idx_out=idx, workspace=ws_i, stream=st)
+        sdi.attend(dev.kv, dev.q, idx, kps, out=out, workspace=ws_a, stream=st)
+        sdi.dense(dev.kv, dev.q, out=dn, workspace=ws_d, stream=st)
+
+    step()
+    torch.cuda.synchronize()
+    want = (idx.clone(), out.clone(), dn.clone())
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        step()
+    for rep in range(4):
+        idx.fill_(-7); out.fill_(float("nan")); dn.fill_(float("nan"))
+        ws_i.fill_(0xAB)                                     # stale scratch must not matter
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        _say(f"[graph] replay {rep}")
+        assert torch.equal(idx, want[0]) and torch.equal(out, want[1]) and torch.equal(dn, want[2]), rep
