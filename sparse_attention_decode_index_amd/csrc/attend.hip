@@ -9,42 +9,46 @@
 // 5.1) in fp32, split over chunks of the index list, and the chunk partials are
 // combined by merge_kernel with a log-sum-exp merge.
 //
-// Work decomposition: a workgroup of 4 waves takes 256 consecutive entries of one
-// (b, h) index row; each wave takes 64.  Inside a wave, each group of 16 lanes owns
-// one gathered row at a time (16 lanes x 16 B = the 256 B row, one 128-bit load
-// per lane for K and one for V), 8 rows per group are in flight at once, and each
-// group keeps its own running softmax state; the 4 groups, then the 4 waves, are
+// Work decomposition: a workgroup of W waves (W = min(16, ceil(k_max / 64))) takes
+// 64 W consecutive entries of one (b, h) index row, 64 per wave, so rows with
+// k <= 1024 need no second launch.  Inside a wave, each group of 16 lanes owns one
+// gathered row at a time (16 lanes x 16 B = the 256 B row, one 128-bit load per
+// lane for K and one for V); 8 rows of a group are in flight at once, and each
+// group keeps its own running softmax state; the 4 groups, then the W waves, are
 // merged at the end.
 #include "sdi_device.hpp"
 #include "sdi_launch.hpp"
 
 namespace sdi {
 
-constexpr int kAttWaves = 4;
+constexpr int kAttMaxWaves = 16;
 constexpr int kAttPerWave = 64;
-constexpr int kAttPerBlock = kAttWaves * kAttPerWave;   // 256 index entries per workgroup
 constexpr int kAttBatch = 8;                            // rows per 16-lane group in flight
+
+int attend_waves(int k_max) { return std::min(kAttMaxWaves, (k_max + kAttPerWave - 1) / kAttPerWave); }
 constexpr float kLog2e = 1.4426950408889634f;
 
-// grid (splits, num_q_heads, batch); 256 threads.
-__global__ __launch_bounds__(kAttWaves * 64) void attend_kernel(
+// grid (splits, num_q_heads, batch); 64 W threads.
+__global__ __launch_bounds__(kAttMaxWaves * 64) void attend_kernel(
     const uint16_t *__restrict__ kc, const uint16_t *__restrict__ vc, const int32_t *__restrict__ page_table,
     const int32_t *__restrict__ seq_lens, const uint16_t *__restrict__ q, const int32_t *__restrict__ idx,
     const int32_t *__restrict__ k_per_seq, int num_q_heads, int num_kv_heads, int group, int max_pages, int k_max,
     float scale_log2, int splits, float *__restrict__ part_ml, float *__restrict__ part_acc,
     float *__restrict__ out)
 {
-    __shared__ float red_acc[kAttWaves][kHeadDim];
-    __shared__ float red_ml[kAttWaves][2];
+    __shared__ float red_acc[kAttMaxWaves][kHeadDim];
+    __shared__ float red_ml[kAttMaxWaves][2];
+    const int waves = blockDim.x >> 6;
     const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int64_t bh = (int64_t)b * num_q_heads + h;
     const int g = h / group;
     const int n = seq_lens[b];
     int kk = k_per_seq ? min(k_per_seq[b], k_max) : k_max;
     if (kk < 0) kk = 0;
-    const int i0 = split * kAttPerBlock;
+    const int i0 = split * waves * kAttPerWave;
     if (i0 >= kk) {                          // nothing listed in this chunk
-        if (splits == 1 && threadIdx.x < kHeadDim) out[bh * kHeadDim + threadIdx.x] = 0.f;
+        if (splits == 1)
+            for (int t = threadIdx.x; t < kHeadDim; t += blockDim.x) out[bh * kHeadDim + t] = 0.f;
         return;                              // (chunks past k are never merged)
     }
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -86,8 +90,8 @@ __global__ __launch_bounds__(kAttWaves * 64) void attend_kernel(
             vw[r] = u32x4{0u, 0u, 0u, 0u};
             if (rows[r] >= 0) {
                 const int64_t off = (int64_t)rows[r] * kHeadDim + sub * 8;
-                kw[r] = *(const u32x4 *)(kc + off);
-                vw[r] = *(const u32x4 *)(vc + off);
+                kw[r] = __builtin_nontemporal_load((const u32x4 *)(kc + off));
+                vw[r] = __builtin_nontemporal_load((const u32x4 *)(vc + off));
             }
         }
         float x[kAttBatch];
@@ -143,15 +147,12 @@ __global__ __launch_bounds__(kAttWaves * 64) void attend_kernel(
     }
     __syncthreads();
 
-    // Merge the 4 waves; thread t < 128 owns output dim t.
-    if (threadIdx.x < kHeadDim) {
-        const int t = threadIdx.x;
+    // Merge the waves; thread t owns output dims t, t + blockDim.x, ... (one wave has 64 threads).
+    for (int t = threadIdx.x; t < kHeadDim; t += blockDim.x) {
         float Mw = red_ml[0][0];
-#pragma unroll
-        for (int w = 1; w < kAttWaves; ++w) Mw = fmaxf(Mw, red_ml[w][0]);
+        for (int w = 1; w < waves; ++w) Mw = fmaxf(Mw, red_ml[w][0]);
         float L = 0.f, A = 0.f;
-#pragma unroll
-        for (int w = 0; w < kAttWaves; ++w) {
+        for (int w = 0; w < waves; ++w) {
             const float fw = (Mw == -INFINITY) ? 0.f : fast_exp2(red_ml[w][0] - Mw);
             L += fw * red_ml[w][1];
             A += fw * red_acc[w][t];
@@ -168,32 +169,77 @@ __global__ __launch_bounds__(kAttWaves * 64) void attend_kernel(
 
 // Log-sum-exp merge of per-chunk partials (m, l, acc[128]) of each (b, h).
 // live chunks = ceil(count / per_chunk) with count = min(k_b, k_max) (sparse) or N_b
-// (dense).  grid (num_q_heads, batch); 128 threads, thread t owns dim t.
-__global__ __launch_bounds__(kHeadDim) void merge_kernel(const float *__restrict__ part_ml,
-                                                         const float *__restrict__ part_acc, int splits,
-                                                         int per_chunk, const int32_t *__restrict__ counts,
-                                                         int count_cap, int num_q_heads, float *__restrict__ out)
+// (dense).  grid (num_q_heads, batch); 512 threads: the chunk weights
+// e^{m_s - M} are computed once into LDS, then 4 groups of 128 threads (one dim
+// each) sum over interleaved chunks and combine their sums in LDS.
+constexpr int kMergeThreads = 512;
+constexpr int kMergeGroups = kMergeThreads / kHeadDim;
+constexpr int kMergeWeights = 4096;                       // chunk weights kept in LDS
+
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float *__restrict__ part_ml,
+                                                              const float *__restrict__ part_acc, int splits,
+                                                              int per_chunk, const int32_t *__restrict__ counts,
+                                                              int count_cap, int num_q_heads, float *__restrict__ out)
 {
+    __shared__ float wts[kMergeWeights];
+    __shared__ float red[kMergeThreads / 64];
+    __shared__ float gsum[kMergeGroups][kHeadDim];
     const int h = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
+    const int lane = t & 63, wave = t >> 6;
     const int64_t bh = (int64_t)b * num_q_heads + h;
     int cnt = counts ? min(counts[b], count_cap) : count_cap;
     if (cnt < 0) cnt = 0;
     const int live = min(splits, (cnt + per_chunk - 1) / per_chunk);
-    float M = -INFINITY;
-    for (int s = 0; s < live; ++s) M = fmaxf(M, part_ml[(bh * splits + s) * 2]);
-    float L = 0.f, A = 0.f;
-    if (M != -INFINITY) {
-        for (int s = 0; s < live; ++s) {
-            const int64_t ps = bh * splits + s;
-            const float f = fast_exp2(part_ml[ps * 2] - M);
-            L += f * part_ml[ps * 2 + 1];
-            A += f * part_acc[ps * kHeadDim + t];
-        }
+    const float *ml = part_ml + bh * splits * 2;
+
+    // M = max of the chunk maxima
+    float m = -INFINITY;
+    for (int s = t; s < live; s += kMergeThreads) m = fmaxf(m, ml[2 * s]);
+    for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+    if (lane == 0) red[wave] = m;
+    __syncthreads();
+    float M = red[0];
+#pragma unroll
+    for (int w = 1; w < kMergeThreads / 64; ++w) M = fmaxf(M, red[w]);
+    __syncthreads();
+
+    // weights and L = sum_s e^{m_s - M} l_s
+    float l = 0.f;
+    for (int s = t; s < live; s += kMergeThreads) {
+        const float f = (M == -INFINITY) ? 0.f : fast_exp2(ml[2 * s] - M);
+        if (s < kMergeWeights) wts[s] = f;
+        l += f * ml[2 * s + 1];
     }
-    out[bh * kHeadDim + t] = L > 0.f ? A / L : 0.f;
+    for (int o = 32; o > 0; o >>= 1) l += __shfl_xor(l, o, 64);
+    if (lane == 0) red[wave] = l;
+    __syncthreads();
+    float L = 0.f;
+#pragma unroll
+    for (int w = 0; w < kMergeThreads / 64; ++w) L += red[w];
+
+    // accumulators: group j sums chunks j, j + 4, ...
+    const int d = t % kHeadDim, grp = t / kHeadDim;
+    const float *pa = part_acc + bh * splits * kHeadDim + d;
+    float A = 0.f;
+    for (int s = grp; s < live; s += kMergeGroups) {
+        const float f = s < kMergeWeights ? wts[s] : ((M == -INFINITY) ? 0.f : fast_exp2(ml[2 * s] - M));
+        A = fmaf(f, pa[(int64_t)s * kHeadDim], A);
+    }
+    gsum[grp][d] = A;
+    __syncthreads();
+    if (t < kHeadDim) {
+        float tot = 0.f;
+#pragma unroll
+        for (int j = 0; j < kMergeGroups; ++j) tot += gsum[j][t];
+        out[bh * kHeadDim + t] = L > 0.f ? tot / L : 0.f;
+    }
 }
 
-int attend_splits(int k_max) { return (k_max + kAttPerBlock - 1) / kAttPerBlock; }
+int attend_splits(int k_max)
+{
+    const int per_block = attend_waves(k_max) * kAttPerWave;
+    return (k_max + per_block - 1) / per_block;
+}
 
 size_t attend_workspace_bytes(int batch, int num_q_heads, int k_max)
 {
@@ -206,8 +252,8 @@ hipError_t launch_merge(const float *part_ml, const float *part_acc, int splits,
                         const int32_t *counts, int count_cap, int batch, int num_q_heads, float *out,
                         hipStream_t stream)
 {
-    hipLaunchKernelGGL(merge_kernel, dim3(num_q_heads, batch), dim3(kHeadDim), 0, stream, part_ml, part_acc, splits,
-                       per_chunk, counts, count_cap, num_q_heads, out);
+    hipLaunchKernelGGL(merge_kernel, dim3(num_q_heads, batch), dim3(kMergeThreads), 0, stream, part_ml, part_acc,
+                       splits, per_chunk, counts, count_cap, num_q_heads, out);
     return hipGetLastError();
 }
 
@@ -218,14 +264,15 @@ hipError_t launch_attend(const AttendArgs &a, hipStream_t stream)
     const size_t bhs = (size_t)a.batch * a.num_q_heads * splits;
     float *part_acc = (float *)a.ws;
     float *part_ml = splits > 1 ? part_acc + bhs * kHeadDim : nullptr;
-    hipLaunchKernelGGL(attend_kernel, dim3(splits, a.num_q_heads, a.batch), dim3(kAttWaves * 64), 0, stream,
+    const int waves = attend_waves(a.k_max);
+    hipLaunchKernelGGL(attend_kernel, dim3(splits, a.num_q_heads, a.batch), dim3(waves * 64), 0, stream,
                        (const uint16_t *)a.k_cache, (const uint16_t *)a.v_cache, a.page_table, a.seq_lens,
                        (const uint16_t *)a.q, a.idx, a.k_per_seq, a.num_q_heads, a.num_kv_heads, group, a.max_pages,
                        a.k_max, a.scale * kLog2e, splits, part_ml, part_acc, a.out);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || splits == 1) return e;
-    return launch_merge(part_ml, part_acc, splits, kAttPerBlock, a.k_per_seq, a.k_max, a.batch, a.num_q_heads,
-                        a.out, stream);
+    return launch_merge(part_ml, part_acc, splits, waves * kAttPerWave, a.k_per_seq, a.k_max, a.batch,
+                        a.num_q_heads, a.out, stream);
 }
 
 }  // namespace sdi

@@ -53,9 +53,9 @@ def test_workspace_sizes(lib):
     k = kv()
     n1 = lib.sparse_decode_index_topk_workspace(ctypes.byref(k), 8, 5)
     assert n1 == 2 * 8 * (256 * 6 + 4096 * 4)            # per row: 32-bit keys + 16-bit codes (padded to 128) + histogram
-    assert lib.sparse_decode_attend_workspace(ctypes.byref(k), 8, 256) == 0          # one chunk: no partials
-    assert lib.sparse_decode_attend_workspace(ctypes.byref(k), 8, 257) == 2 * 8 * 2 * 130 * 4
-    assert lib.dense_decode_workspace(ctypes.byref(k), 8) == 2 * 8 * 2 * 130 * 4
+    assert lib.sparse_decode_attend_workspace(ctypes.byref(k), 8, 1024) == 0         # one chunk: no partials
+    assert lib.sparse_decode_attend_workspace(ctypes.byref(k), 8, 1025) == 2 * 8 * 2 * 130 * 4
+    assert lib.dense_decode_workspace(ctypes.byref(k), 8) == 2 * 8 * 1 * 130 * 4      # one 1024-token chunk
     assert lib.sparse_decode_attend_workspace(None, 8, 5) == 0
 
 
@@ -117,9 +117,9 @@ def test_argument_errors(lib):
     assert call_attend(lib, k, out=None) == sdi.SDI_ERR_NULL
     assert call_attend(lib, k, k_max=0) == sdi.SDI_ERR_K
     assert call_attend(lib, k, hq=3) == sdi.SDI_ERR_SHAPE
-    need = lib.sparse_decode_attend_workspace(ctypes.byref(k), 8, 1000)
-    assert need > 0 and call_attend(lib, k, k_max=1000, nbytes=need - 1) == sdi.SDI_ERR_WORKSPACE
-    assert call_attend(lib, k, k_max=1000, ws=None) == sdi.SDI_ERR_NULL
+    need = lib.sparse_decode_attend_workspace(ctypes.byref(k), 8, 2000)
+    assert need > 0 and call_attend(lib, k, k_max=2000, nbytes=need - 1) == sdi.SDI_ERR_WORKSPACE
+    assert call_attend(lib, k, k_max=2000, ws=None) == sdi.SDI_ERR_NULL
     assert call_dense(lib, k, out=None) == sdi.SDI_ERR_NULL
     need = lib.dense_decode_workspace(ctypes.byref(k), 8)
     assert call_dense(lib, k, nbytes=need - 1) == sdi.SDI_ERR_WORKSPACE
