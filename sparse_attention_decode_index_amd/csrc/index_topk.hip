@@ -18,16 +18,17 @@
 //                    writes with the K stream is what costs bandwidth, and 16-bit
 //                    codes halve it.  The top 12 code bits are counted into an LDS
 //                    histogram per head, flushed with integer atomics.
-//  3. select_kernel  per (b, h): the 12-bit histogram plus a 4-bit histogram of the
-//                    codes in the threshold bin give the code c* holding the k-th
-//                    key; one ordered-compaction pass
-//                    lists the tokens above c* (all selected) and the tokens with
-//                    code c*; the exact keys of the latter are recomputed with the
-//                    same MFMA sequence (bit-identical), an 8+8-bit radix on their
-//                    low halves gives the exact threshold, and the two ascending
-//                    lists are merged into the output.  If either list outgrows
-//                    LDS, the head is re-scored to full 32-bit keys in the
-//                    workspace and a generic radix select runs over them.
+//  3. select_kernel  per (b, h): the 12-bit histogram gives the bin b* holding the
+//                    k-th key; ONE ordered-compaction pass over the codes lists
+//                    the tokens above b* (all selected) and the tokens inside b*
+//                    with their codes, in LDS.  A 4-bit histogram of the latter
+//                    gives the code c* of the k-th key; the exact keys of the
+//                    tokens with code c* are recomputed with the same MFMA sequence
+//                    (bit-identical); an 8+8-bit radix on their low halves gives
+//                    the exact threshold; the selected part of the bin list is
+//                    compacted and merged with the above list into the output.  If
+//                    a list outgrows LDS, the head is re-scored to full 32-bit keys
+//                    in the workspace and a generic radix select runs over them.
 #include "sdi_device.hpp"
 #include "sdi_launch.hpp"
 
@@ -55,12 +56,13 @@ __global__ void zero_hist_kernel(uint32_t *__restrict__ p, int64_t n)
 }
 
 // ---- select ------------------------------------------------------------------------------
-constexpr int kSelThreads = 1024;
+constexpr int kSelThreads = 512;
 constexpr int kSelWaves = kSelThreads / 64;
 constexpr int kSelCodesPerThread = 32;                        // 64 B of codes per thread per round
 constexpr int kSelRound = kSelThreads * kSelCodesPerThread;   // 32768 tokens
-constexpr int kSelACap = 8192;                                // tokens above the threshold code
-constexpr int kSelCCap = 2048;                                // tokens sharing the threshold code
+constexpr int kSelACap = 8192;                                // tokens above the threshold bin
+constexpr int kSelCCap = 4096;                                // tokens in the threshold's 12-bit bin
+constexpr int kSelECap = 2048;                                // of those, tokens with the threshold code
 constexpr int kSelPerThread = 8;                              // generic path
 constexpr int kSelTile = kSelThreads * kSelPerThread;
 
@@ -335,7 +337,7 @@ __device__ __forceinline__ f32x4 rescore16(const uint16_t *__restrict__ kc, int 
 
 // Generic select over full 32-bit keys in memory: 12 + 10 + 10-bit radix passes,
 // then one ordered-compaction pass writes the selection.
-__device__ void select_generic(const uint32_t *__restrict__ kh, int n, int kk, int k_max, uint32_t *hist,
+__device__ __forceinline__ void select_generic(const uint32_t *__restrict__ kh, int n, int kk, int k_max, uint32_t *hist,
                                uint32_t *scratch, uint32_t *res, int32_t *__restrict__ out)
 {
     uint32_t prefix = 0, need = (uint32_t)kk;
@@ -407,16 +409,48 @@ struct SelectArgs {
     int32_t *idx_out;
 };
 
-// grid (num_q_heads, batch); 1024 threads.
+// Generic path for one head: re-score every token to its full 32-bit key in the
+// workspace row, then radix-select over the keys.  Called by the whole workgroup.
+__device__ __forceinline__ void select_rescore_generic(const SelectArgs &a, int64_t bh, int b, int g, int hb, int hn,
+                                       int heads_here, int n, int kk, uint32_t *hist, uint32_t *scratch,
+                                       uint32_t *res, int32_t *__restrict__ out)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int col = lane & 15, quad = lane >> 4;
+    uint32_t *krow = a.keys32 + bh * a.stride;
+    const int32_t *pt = a.page_table + (int64_t)b * a.max_pages;
+    bf16x8 qb[4];
+    load_q_operand(qb, a.q, (int64_t)b * a.num_q_heads + g * a.group + hb * kHeadBlock, heads_here, col, quad);
+    for (int t0 = wave * 16; t0 < n; t0 += kSelWaves * 16) {
+        const int tok = t0 + col;
+        const int row = tok < n ? (pt[tok >> 4] * a.num_kv_heads + g) * kPage + (tok & 15) : -1;
+        const f32x4 acc = rescore16(a.kc, row, qb, quad);
+        if (col == hn) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (t0 + 4 * quad + i < n) krow[t0 + 4 * quad + i] = score_key(acc[i]);
+        }
+    }
+    __threadfence_block();
+    __syncthreads();
+    select_generic(krow, n, kk, a.k_max, hist, scratch, res, out);
+}
+
+// grid (num_q_heads, batch); kSelThreads threads.
 __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a)
 {
-    __shared__ uint32_t whist[kSelWaves * 256];               // digit 1 per wave; later other histograms
-    __shared__ uint32_t hist2[256];
-    __shared__ uint32_t A[kSelACap];                          // tokens above the threshold code
-    __shared__ uint32_t Ci[kSelCCap];                         // tokens with the threshold code
-    __shared__ uint32_t Ck[kSelCCap];                         // their exact keys
+    __shared__ uint32_t whist[kHistBins];                     // digit-1 histogram, then scratch lists
+    __shared__ uint32_t A[kSelACap];                          // tokens above the threshold bin
+    __shared__ uint32_t Ci[kSelCCap];                         // tokens inside the bin (compacted in place later)
+    __shared__ uint16_t Cc[kSelCCap];                         // their codes
+    __shared__ uint32_t hist16[16];
     __shared__ uint32_t scratch[kSelWaves + 2];
     __shared__ uint32_t res[8];
+    uint32_t *Ek = whist;                                     // exact keys of the tokens with code c* (kSelECap)
+    uint16_t *Ep = (uint16_t *)(whist + kSelECap);            // their positions in C (kSelECap)
+    uint32_t *hist3 = whist + kSelECap + kSelECap / 2;        // 256
+    uint32_t *hist4 = hist3 + 256;                            // 256
+
     const int h = blockIdx.x, b = blockIdx.y;
     const int64_t bh = (int64_t)b * a.num_q_heads + h;
     const int n = a.seq_lens[b];
@@ -431,7 +465,6 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a)
     const int col = lane & 15, quad = lane >> 4;
     const int g = h / a.group, hl = h - g * a.group, hb = hl / kHeadBlock, hn = hl - hb * kHeadBlock;
     const int heads_here = min(kHeadBlock, a.group - hb * kHeadBlock);
-    const int64_t q_row0 = (int64_t)b * a.num_q_heads + g * a.group + hb * kHeadBlock;
     const int32_t *pt = a.page_table + (int64_t)b * a.max_pages;
     const uint16_t *crow = a.codes + bh * a.stride;
     const int rounds = (n + kSelRound - 1) / kSelRound;
@@ -439,61 +472,36 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a)
     u32x4 w[4];
     int cnt = load_codes(crow, threadIdx.x * kSelCodesPerThread, n, w);
     for (int i = threadIdx.x; i < kHistBins; i += kSelThreads) whist[i] = a.ghist[bh * kHistBins + i];
-    if (threadIdx.x < 256) hist2[threadIdx.x] = 0u;
+    if (threadIdx.x < 16) hist16[threadIdx.x] = 0u;
     if (threadIdx.x < 8) res[threadIdx.x] = 0u;
     __syncthreads();
-    // digit 1 (code bits 15..4) was counted by the score pass
+    // 1. the 12-bit bin b* holding the k-th key (histogram from the score pass)
     threshold_bin_wave(whist, kHistBins, (uint32_t)kk, res);
-    const uint32_t d1 = res[0], above1 = res[1];
-    // digit 2 (code bits 3..0) among codes whose digit 1 is d1
-    for (int r = 0; r < rounds; ++r) {
-        if (rounds > 1) cnt = load_codes(crow, r * kSelRound + threadIdx.x * kSelCodesPerThread, n, w);
-#pragma unroll
-        for (int e = 0; e < kSelCodesPerThread; ++e) {
-            const uint32_t c = code_at(w, e);
-            if (e < cnt && (c >> 4) == d1) atomicAdd(&hist2[c & 15u], 1u);
-        }
-    }
-    __syncthreads();
-    threshold_bin_wave(hist2, 64, (uint32_t)kk - above1, res + 2);   // bins 16..63 are empty
-    const uint32_t cstar = (d1 << 4) | res[2];
-    const uint32_t above = above1 + res[3];
-    const uint32_t in_bin = hist2[res[2]];
-    uint32_t need = (uint32_t)kk - above;                     // >= 1 of the in_bin tokens
-
+    const uint32_t bstar = res[0], above = res[1];
+    const uint32_t in_bin = whist[bstar];
     if (above > (uint32_t)kSelACap || in_bin > (uint32_t)kSelCCap) {
-        // Generic path: re-score this head to full keys, then radix-select over them.
-        uint32_t *krow = a.keys32 + bh * a.stride;
-        bf16x8 qb[4];
-        load_q_operand(qb, a.q, q_row0, heads_here, col, quad);
-        for (int t0 = wave * 16; t0 < n; t0 += kSelWaves * 16) {
-            const int tok = t0 + col;
-            const int row = tok < n ? (pt[tok >> 4] * a.num_kv_heads + g) * kPage + (tok & 15) : -1;
-            const f32x4 acc = rescore16(a.kc, row, qb, quad);
-            if (col == hn) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    if (t0 + 4 * quad + i < n) krow[t0 + 4 * quad + i] = score_key(acc[i]);
-            }
-        }
-        __threadfence_block();
-        __syncthreads();
-        select_generic(krow, n, kk, a.k_max, whist, scratch, res, out);
+        __syncthreads();                                      // everyone has read res and whist[b*]
+        select_rescore_generic(a, bh, b, g, hb, hn, heads_here, n, kk, whist, scratch, res, out);
         return;
     }
 
-    // ordered compaction: A = tokens with code > c*, C = tokens with code == c*
+    // 2. one pass: A = tokens above b*, C = tokens inside b* (+ their codes and a 4-bit histogram)
     uint32_t run_a = 0, run_c = 0;
     for (int r = 0; r < rounds; ++r) {
         const int start = r * kSelRound + threadIdx.x * kSelCodesPerThread;
-        if (rounds > 1) cnt = load_codes(crow, start, n, w);
+        u32x4 wn[4];
+        int cnt_n = 0;
+        if (r + 1 < rounds) cnt_n = load_codes(crow, start + kSelRound, n, wn);   // next round in flight
         uint32_t ma = 0, mc = 0;
+        uint32_t nib[4] = {0u, 0u, 0u, 0u};                   // low 4 code bits, 8 tokens per word
 #pragma unroll
         for (int e = 0; e < kSelCodesPerThread; ++e) {
-            const uint32_t c = code_at(w, e);
-            ma |= (e < cnt && c > cstar) ? (1u << e) : 0u;
-            mc |= (e < cnt && c == cstar) ? (1u << e) : 0u;
+            const uint32_t c = code_at(w, e), d = c >> 4;
+            ma |= (e < cnt && d > bstar) ? (1u << e) : 0u;
+            mc |= (e < cnt && d == bstar) ? (1u << e) : 0u;
+            nib[e >> 3] |= (c & 15u) << (4 * (e & 7));
         }
+        const uint32_t n0 = nib[0], n1 = nib[1], n2 = nib[2], n3 = nib[3];
         uint32_t tot;
         const uint32_t pre = block_exclusive_scan<kSelThreads>(((uint32_t)__popc(mc) << 16) | (uint32_t)__popc(ma),
                                                                scratch, tot);
@@ -507,87 +515,137 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a)
         while (mc) {
             const int e = __builtin_ctz(mc);
             mc &= mc - 1u;
-            if (pc < (uint32_t)kSelCCap) Ci[pc] = (uint32_t)(start + e);
+            const int q8 = e >> 3;                              // scalars, not an indexed array
+            const uint32_t nw = q8 == 0 ? n0 : q8 == 1 ? n1 : q8 == 2 ? n2 : n3;
+            const uint32_t c = (bstar << 4) | ((nw >> (4 * (e & 7))) & 15u);
+            if (pc < (uint32_t)kSelCCap) { Ci[pc] = (uint32_t)(start + e); Cc[pc] = (uint16_t)c; }
             ++pc;
+            atomicAdd(&hist16[c & 15u], 1u);
         }
         run_a += tot & 0xFFFFu;
         run_c += tot >> 16;
+        if (r + 1 < rounds) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) w[i] = wn[i];
+            cnt = cnt_n;
+        }
     }
     __syncthreads();
     const int na_tot = (int)min(run_a, (uint32_t)kSelACap);
     const int m = (int)min(run_c, (uint32_t)kSelCCap);
 
-    // exact keys of C: 16 candidates per MFMA group, one group per wave at a time
+    // 3. wave 0: the code c* of the k-th key (4-bit digit), then the list E of bin
+    //    entries with code c*, in order.
+    if (threadIdx.x < 64) {
+        const uint32_t need1 = (uint32_t)kk - above;
+        uint32_t d2 = 0, ab2 = 0;
+        // 16 bins, highest first: lane l < 16 looks at bin 15 - l
+        const uint32_t cnt2 = lane < 16 ? hist16[15 - lane] : 0u;
+        const uint32_t x = wave_inclusive_scan(cnt2);
+        const uint64_t cross = __ballot(lane < 16 && x >= need1);
+        if (cross) {
+            const int L = __ffsll((unsigned long long)cross) - 1;
+            d2 = (uint32_t)(15 - L);
+            ab2 = __shfl(x - cnt2, L, 64);
+        }
+        const uint32_t cstar = (bstar << 4) | d2;
+        uint32_t me = 0;
+        for (int i0 = 0; i0 < m; i0 += 64) {
+            const int i = i0 + lane;
+            const bool eq = i < m && Cc[i] == cstar;
+            const uint64_t bal = __ballot(eq);
+            const uint32_t before = (uint32_t)__popcll(bal & ((1ull << lane) - 1ull));
+            if (eq && me + before < (uint32_t)kSelECap) Ep[me + before] = (uint16_t)i;
+            me += (uint32_t)__popcll(bal);
+        }
+        if (lane == 0) { res[2] = cstar; res[3] = need1 - ab2; res[4] = me; }
+    }
+    __syncthreads();
+    const uint32_t cstar = res[2];
+    uint32_t need = res[3];                                   // >= 1 of the tokens with code c*
+    const int me = (int)res[4];
+    if (me > kSelECap) {
+        __syncthreads();
+        select_rescore_generic(a, bh, b, g, hb, hn, heads_here, n, kk, whist, scratch, res, out);
+        return;
+    }
+
+    // 4. exact keys of E (16 per MFMA group, all waves)
     {
         bf16x8 qb[4];
-        load_q_operand(qb, a.q, q_row0, heads_here, col, quad);
-        for (int c0 = wave * 16; c0 < m; c0 += kSelWaves * 16) {
+        load_q_operand(qb, a.q, (int64_t)b * a.num_q_heads + g * a.group + hb * kHeadBlock, heads_here, col, quad);
+        for (int c0 = wave * 16; c0 < me; c0 += kSelWaves * 16) {
             int row = -1;
-            if (c0 + col < m) {
-                const int tok = (int)Ci[c0 + col];
+            if (c0 + col < me) {
+                const int tok = (int)Ci[Ep[c0 + col]];
                 row = (pt[tok >> 4] * a.num_kv_heads + g) * kPage + (tok & 15);
             }
             const f32x4 acc = rescore16(a.kc, row, qb, quad);
             if (col == hn) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    if (c0 + 4 * quad + i < m) Ck[c0 + 4 * quad + i] = score_key(acc[i]);
+                    if (c0 + 4 * quad + i < me) Ek[c0 + 4 * quad + i] = score_key(acc[i]);
             }
         }
     }
-    if (threadIdx.x < 256) { whist[threadIdx.x] = 0u; hist2[threadIdx.x] = 0u; }
+    if (threadIdx.x < 512) hist3[threadIdx.x] = 0u;           // hist3 and hist4
     __syncthreads();
 
-    // Exact threshold inside C and the selected candidates, by wave 0 alone:
-    // key bits 15..8, then 7..0 (bits 31..16 are c*); then keep key > T, or key == T
-    // among the first r, in token order, into Cs.
-    uint32_t *Cs = whist + 1024;                              // up to kSelCCap selected candidates
+    // 5. wave 0: exact threshold among E (key bits 15..8, then 7..0), flags of the
+    //    selected E entries, then the selected bin entries compacted in place, in order.
     if (threadIdx.x < 64) {
-        for (int i = lane; i < m; i += 64) atomicAdd(&whist[(Ck[i] >> 8) & 255u], 1u);
+        for (int i = lane; i < me; i += 64) atomicAdd(&hist3[(Ek[i] >> 8) & 255u], 1u);
         wave_lds_sync();
         uint32_t d3 = 0, ab3 = 0;
-        wave_threshold(whist, 256, need, d3, ab3);
+        wave_threshold(hist3, 256, need, d3, ab3);
         need -= ab3;
         const uint32_t pref3 = (cstar << 8) | d3;
-        for (int i = lane; i < m; i += 64)
-            if ((Ck[i] >> 8) == pref3) atomicAdd(&hist2[Ck[i] & 255u], 1u);
+        for (int i = lane; i < me; i += 64)
+            if ((Ek[i] >> 8) == pref3) atomicAdd(&hist4[Ek[i] & 255u], 1u);
         wave_lds_sync();
         uint32_t d4 = 0, ab4 = 0;
-        wave_threshold(hist2, 256, need, d4, ab4);
+        wave_threshold(hist4, 256, need, d4, ab4);
         need -= ab4;
         const uint32_t T = (pref3 << 8) | d4, r = need;
-        const int per = (m + 63) / 64;                        // entries owned by each lane, in order
-        uint32_t gt = 0, eq = 0;
-        for (int e = 0; e < per; ++e) {
-            const int i = lane * per + e;
-            if (i < m) { gt += Ck[i] > T ? 1u : 0u; eq += Ck[i] == T ? 1u : 0u; }
+        // flags in E order: key > T, or key == T among the first r
+        uint32_t eq_run = 0;
+        for (int i0 = 0; i0 < me; i0 += 64) {
+            const int i = i0 + lane;
+            const uint32_t k = i < me ? Ek[i] : 0u;
+            const bool is_eq = i < me && k == T;
+            const uint64_t bal = __ballot(is_eq);
+            const uint32_t rank = eq_run + (uint32_t)__popcll(bal & ((1ull << lane) - 1ull));
+            if (i < me) Ek[i] = (k > T || (is_eq && rank < r)) ? 1u : 0u;
+            eq_run += (uint32_t)__popcll(bal);
         }
-        const uint32_t inc = wave_inclusive_scan((eq << 16) | gt);
-        const uint32_t pre = inc - ((eq << 16) | gt);
-        uint32_t pos = (pre & 0xFFFFu) + min(pre >> 16, r);
-        uint32_t eq_rank = pre >> 16;
-        for (int e = 0; e < per; ++e) {
-            const int i = lane * per + e;
-            if (i < m) {
-                const uint32_t k = Ck[i];
-                bool take = k > T;
-                if (k == T) take = (eq_rank++ < r);
-                if (take) Cs[pos++] = Ci[i];
-            }
+        wave_lds_sync();
+        // compact C in place: keep code > c*, or code == c* with its E flag set
+        uint32_t kept = 0, e_run = 0;
+        for (int i0 = 0; i0 < m; i0 += 64) {
+            const int i = i0 + lane;
+            const uint32_t c = i < m ? Cc[i] : 0u;
+            const bool is_eq = i < m && c == cstar;
+            const uint64_t beq = __ballot(is_eq);
+            const uint32_t eidx = e_run + (uint32_t)__popcll(beq & ((1ull << lane) - 1ull));
+            const bool keep = i < m && (c > cstar || (is_eq && Ek[eidx] != 0u));
+            const uint64_t bk = __ballot(keep);
+            const uint32_t tok = i < m ? Ci[i] : 0u;                 // read before this row is written
+            if (keep) Ci[kept + (uint32_t)__popcll(bk & ((1ull << lane) - 1ull))] = tok;
+            kept += (uint32_t)__popcll(bk);
+            e_run += (uint32_t)__popcll(beq);
         }
-        const uint32_t all = __shfl(inc, 63, 64);
-        if (lane == 0) res[0] = min((all & 0xFFFFu) + min(all >> 16, r), (uint32_t)m);
+        if (lane == 0) res[5] = kept;
     }
     __syncthreads();
-    const int ns = (int)res[0];                               // selected candidates
+    const int ns = (int)res[5];                               // selected bin entries, ascending in Ci
 
-    // merge the two ascending lists into the output row
+    // 6. merge the two ascending lists into the output row
     for (int i = threadIdx.x; i < na_tot; i += kSelThreads) {
         const uint32_t x = A[i];
-        out[i + count_below(Cs, ns, x)] = (int32_t)x;
+        out[i + count_below(Ci, ns, x)] = (int32_t)x;
     }
     for (int j = threadIdx.x; j < ns; j += kSelThreads) {
-        const uint32_t x = Cs[j];
+        const uint32_t x = Ci[j];
         out[j + count_below(A, na_tot, x)] = (int32_t)x;
     }
     for (int i = na_tot + ns + threadIdx.x; i < a.k_max; i += kSelThreads) out[i] = -1;
