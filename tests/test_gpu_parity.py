@@ -285,6 +285,53 @@ def test_select_fallback_paths():
                   tag="fallback")
 
 
+def test_select_sample_bound_too_high():
+    """Every page the sampling pass looks at (one in four here) holds high scores and
+    the other pages low ones, so the sample's lower bound is reached by fewer than k
+    tokens of the row; the select must notice and still return the exact top k."""
+    rng = np.random.default_rng(12)
+    n, hq = 4096, 4
+    q = bf16_round(rng.standard_normal((1, hq, 128)))
+    u = q[0].sum(axis=0)
+    u /= np.linalg.norm(u)
+    page = np.arange(n) // 16
+    high = (page % 4) == 0
+    k = np.where(high[:, None], 8.0 * u[None, :] + 0.5 * rng.standard_normal((n, 128)),
+                 0.1 * rng.standard_normal((n, 128)))
+    case = TinyCase([bf16_round(k)[None]], [bf16_round(rng.standard_normal((1, n, 128)))], q,
+                    layout="contiguous")
+    dev = DeviceCase.of_tiny(case)
+    cache = oracle.Cache(case.k_cache, case.v_cache, case.page_table, case.lens)
+    gidx, _, _, _ = run_and_check(dev, cache, case.q, np.array([400], np.int32), 400, check_dense=False,
+                                  tag="sample-bound")
+    assert np.all(gidx[0] >= 0)
+
+
+def test_select_block_bound_above_kth():
+    """The first workgroup's sample pages hold the highest keys of the row and the rest
+    of that workgroup low ones, so its bound lies above the k-th key while the other
+    workgroups still deliver enough candidates; the select must detect the bound it
+    cannot trust and still return the exact top k."""
+    rng = np.random.default_rng(13)
+    n, hq = 16384, 4
+    q = bf16_round(rng.standard_normal((1, hq, 128)))
+    u = q[0].sum(axis=0)
+    u /= np.linalg.norm(u)
+    t = np.arange(n)
+    high = (t < 4096) & ((t % 512) < 128)                     # the first workgroup's sample pages
+    low = (t < 4096) & ~high
+    amp = np.where(high, 6.0, np.where(low, 0.0, 3.0))
+    noise = np.where(low, 0.1, 0.3)[:, None] * rng.standard_normal((n, 128))
+    k = amp[:, None] * u[None, :] + noise
+    case = TinyCase([bf16_round(k)[None]], [bf16_round(rng.standard_normal((1, n, 128)))], q,
+                    layout="shuffled")
+    dev = DeviceCase.of_tiny(case)
+    cache = oracle.Cache(case.k_cache, case.v_cache, case.page_table, case.lens)
+    gidx, _, _, _ = run_and_check(dev, cache, case.q, np.array([1000], np.int32), 1000, check_dense=False,
+                                  tag="block-bound")
+    assert np.all(np.isin(np.nonzero(high)[0], gidx[0]))
+
+
 def test_graph_replay_matches_eager():
     """A decode step (index -> attend) and dense decode captured in one HIP graph and
     replayed several times, with eager work and synchronisation between replays:
