@@ -12,7 +12,8 @@
 //                    non-temporal 1 KiB loads, transposes each page through LDS
 //                    into the MFMA operand layout and scores 16 tokens x up to 8
 //                    heads of the GQA group per 4 MFMAs (16x16x32 bf16).  Each
-//                    workgroup first scores 8 pages per wave (1024 tokens per head),
+//                    workgroup (4 waves, 2048 tokens, two per CU) first scores 16
+//                    pages per wave (1024 tokens per head),
 //                    keeps those keys in registers and takes, per head, a sample
 //                    order statistic a safe margin above its share of the k-th key:
 //                    a lower bound `lo` that about 1.5..2.5 k tokens of the row
@@ -45,7 +46,7 @@ namespace sdi {
 constexpr int kHeadBlock = 8;                                 // query heads scored per workgroup
 
 // ---- score pass --------------------------------------------------------------------------
-constexpr int kScoreWaves = 8;
+constexpr int kScoreWaves = 4;                                // two workgroups per CU (LDS < 80 KB each)
 constexpr int kScorePagesPerWave = 32;
 constexpr int kScoreUnroll = 2;                               // pages per register buffer
 constexpr int kWaveTokens = kScorePagesPerWave * kPage;       // 512 tokens: one candidate slot
@@ -53,9 +54,13 @@ constexpr int kScoreTokensPerBlock = kScoreWaves * kWaveTokens;
 constexpr int kStageRow = kRowBytes + 16;                     // padded LDS row: conflict-free both ways
 constexpr int kStagePage = kPage * kStageRow;                 // 4352 B
 constexpr int kCandCap = 128;                                 // candidates kept per (slot, head)
+constexpr int kSubCap = kCandCap / 4;                         // ... as 4 lane lists (one per quad) of 32
+constexpr int kSubStride = kSubCap + 1;                       // padded: lists start in different banks
 constexpr uint32_t kCandOverflow = 0xFFFFFFFFu;               // slot count of an overflowed list
-constexpr int kSamplePagesPerWave = 4 * kScoreUnroll;         // the first pages of each wave ...
+constexpr int kSamplePagesPerWave = 16;                       // the first pages of each wave ...
 constexpr int kBlockSample = kScoreWaves * kSamplePagesPerWave * kPage;   // ... 1024 tokens per head
+constexpr int kSampleGroups = kSamplePagesPerWave / kScoreUnroll;
+static_assert(kSampleGroups % 2 == 0 && kSamplePagesPerWave <= kScorePagesPerWave, "sample = pairs of groups");
 
 
 // ---- select ------------------------------------------------------------------------------
@@ -103,6 +108,11 @@ __device__ __forceinline__ f32x4 rescore16(const uint16_t *__restrict__ kc, int 
     return score_mfma(ka, qb);
 }
 
+// Keeps the instruction scheduler from moving anything across this point: the
+// score pass relies on program order (stage a group, put the next group in flight,
+// then score) so that each wait covers only the group being staged.
+__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
+
 __device__ __forceinline__ void wave_lds_sync()
 {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -148,6 +158,15 @@ __device__ __forceinline__ bool wave_threshold(const uint32_t *hist, int nbins, 
     return true;
 }
 
+// Workgroup barrier that orders LDS only: outstanding global loads stay in flight
+// (a full __syncthreads also waits for every vector memory operation).
+__device__ __forceinline__ void lds_barrier()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Sum of v over the 64 lanes of the wave, in every lane.
 __device__ __forceinline__ uint32_t wave_total(uint32_t v)
 {
@@ -166,8 +185,8 @@ __device__ __forceinline__ void threshold_bin_wave(const uint32_t *hist, int nbi
 
 // ---- 1. score pass -----------------------------------------------------------------------
 
-// grid (ceil(n_max / 4096), kv_heads * head_blocks, batch); 512 threads.
-__global__ __launch_bounds__(kScoreWaves * 64) void score_kernel(
+// grid (ceil(n_max / 2048), kv_heads * head_blocks, batch); 256 threads.
+__global__ __launch_bounds__(kScoreWaves * 64, 2) void score_kernel(
     const uint16_t *__restrict__ kc, const int32_t *__restrict__ page_table,
     const int32_t *__restrict__ seq_lens, const uint16_t *__restrict__ q, const int32_t *__restrict__ k_per_seq,
     int num_q_heads, int num_kv_heads, int group, int head_blocks, int max_pages, int k_max,
@@ -176,10 +195,10 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_kernel(
 {
     __shared__ int32_t pt_lds[kScoreWaves * kScorePagesPerWave];
     __shared__ __attribute__((aligned(16))) unsigned char stage_all[kScoreWaves * kScoreUnroll * kStagePage];
-    __shared__ uint32_t ck_all[kScoreWaves * kHeadBlock * kCandCap];
-    __shared__ uint16_t cp_all[kScoreWaves * kHeadBlock * kCandCap];
+    __shared__ uint32_t ck_all[kScoreWaves * kHeadBlock * 4 * kSubStride];
     __shared__ __attribute__((aligned(16))) uint16_t samp[kHeadBlock][kBlockSample];   // top 16 key bits
     __shared__ uint32_t lo_lds[kHeadBlock];
+    __shared__ __attribute__((aligned(16))) uint16_t q_lds[kHeadBlock * kHeadDim];
     const int b = blockIdx.z;
     const int g = blockIdx.y / head_blocks, hb = blockIdx.y - g * head_blocks;
     const int n = seq_lens[b];
@@ -193,24 +212,29 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_kernel(
     const int col = lane & 15, quad = lane >> 4;
     const bool head_lane = col < heads_here;                  // lanes of column col carry head col
     unsigned char *stage = stage_all + wave * kScoreUnroll * kStagePage;
-    uint32_t *ck = ck_all + wave * kHeadBlock * kCandCap;
-    uint16_t *cp = cp_all + wave * kHeadBlock * kCandCap;
-
-    bf16x8 qb[4];
-    load_q_operand(qb, q, (int64_t)b * num_q_heads + h0, heads_here, col, quad);
+    uint32_t *ck = ck_all + wave * kHeadBlock * 4 * kSubStride;
+    const int my_list = (min(col, kHeadBlock - 1) * 4 + quad) * kSubStride;   // this lane's list (head col, quad)
 
     const int pages_seq = (n + kPage - 1) / kPage;
     const int p_base = tok0 / kPage;                          // first page of this workgroup
     const int p_begin = p_base + wave * kScorePagesPerWave;
     const int p_end = min(p_begin + kScorePagesPerWave, pages_seq);
     const bool has_pages = p_begin < p_end;                   // wave-uniform
-    const int slot_tok0 = p_begin * kPage;
     {
         const int32_t *pt = page_table + (int64_t)b * max_pages;
         const int i = threadIdx.x;
         if (i < kScoreWaves * kScorePagesPerWave && p_base + i < pages_seq) pt_lds[i] = pt[p_base + i];
+        // the head block's q rows (16 B per thread), staged with the page slice
+        if (i < heads_here * (kHeadDim / 8))
+            *(u32x4 *)(q_lds + i * 8) = *(const u32x4 *)(q + ((int64_t)b * num_q_heads + h0) * kHeadDim + i * 8);
     }
-    __syncthreads();                                          // page slice staged
+    __syncthreads();                                          // page slice and q staged
+    // MFMA B operand: lane (col, quad) holds head col's dims 32 s + 8 quad .. +7
+    bf16x8 qb[4];
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4)
+        qb[s4] = head_lane ? *(const bf16x8 *)(q_lds + col * kHeadDim + 32 * s4 + 8 * quad)
+                           : __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
 
     const uint16_t *k_head = kc + (int64_t)g * kPage * kHeadDim;                 // + phys * Hkv * 4 KiB
     const int64_t page_elems = (int64_t)num_kv_heads * kPage * kHeadDim;
@@ -218,8 +242,10 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_kernel(
     const int wr_off = (lane >> 4) * kStageRow + (lane & 15) * 16;
     // MFMA A operand: row col, dims 32 s + 8 quad -> bytes 64 s + 16 quad
     const int rd_off = col * kStageRow + quad * 16;
-    uint32_t cnt = 0;                                         // head col's candidates so far (4 lanes agree)
+    uint32_t cnt = 0;                                         // entries of this lane's list so far
+    uint32_t taken[kScorePagesPerWave * 4 / 32] = {0u, 0u, 0u, 0u};   // tokens this lane took
     uint32_t lo = 0xFFFFFFFFu;                                // head col's bound (set after the sample)
+    float lo_f = __builtin_nanf("");                          // the smallest score whose key reaches lo
 
     auto load_group = [&](u32x4 (&kr)[kScoreUnroll][4], int p) {
         int64_t phys[kScoreUnroll];
@@ -239,97 +265,104 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_kernel(
 #pragma unroll
             for (int s = 0; s < 4; ++s) *(u32x4 *)(stage + u * kStagePage + s * 4 * kStageRow + wr_off) = kr[u][s];
     };
-    auto page_keys = [&](int u, uint32_t (&key)[4]) {
-        bf16x8 ka[4];
+    // MFMA A operands of staged page u, and the raw fp32 scores (as bits) they give:
+    // lane holds tokens 4 quad .. +3 of head col
+    auto read_operands = [&](int u, bf16x8 (&ka)[4]) {
 #pragma unroll
         for (int s = 0; s < 4; ++s) ka[s] = *(const bf16x8 *)(stage + u * kStagePage + s * 64 + rd_off);
+    };
+    auto mfma_scores = [&](const bf16x8 (&ka)[4], uint32_t (&sc)[4]) {
         const f32x4 acc = score_mfma(ka, qb);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) key[i] = score_key(acc[i]);
+        for (int i = 0; i < 4; ++i) sc[i] = __float_as_uint(acc[i]);
     };
-    // append page pp's keys that reach lo to head col's list, in token order: head
-    // col's flags sit in lanes col + 16 q, so per token bit i one ballot, masked to
-    // those lanes (below this quad / all of them)
-    auto append_page = [&](const uint32_t (&key)[4], int pp) {
-        const int t0 = pp * kPage + 4 * quad;
-        uint32_t fm = 0;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) fm |= (head_lane && t0 + i < n && key[i] >= lo) ? (1u << i) : 0u;
-        const uint64_t colmask = 0x0001000100010001ull << col;
-        const uint64_t below = colmask & ((1ull << (16 * quad)) - 1ull);
-        uint32_t pre = 0, tot = 0;
+    auto page_scores = [&](int u, uint32_t (&sc)[4]) {
+        bf16x8 ka[4];
+        read_operands(u, ka);
+        mfma_scores(ka, sc);
+    };
+    // append the scores of page po of the wave (po = 0..31, a compile-time offset) whose
+    // key reaches lo, i.e. score >= lo_f: every head lane keeps its own list of scores
+    // (head col, tokens 4 quad .. +3 of each page), ascending by construction, and
+    // marks the tokens it took in a 128-bit mask (bit 4 po + i); the flush recovers
+    // each entry's token from the mask, merges the 4 lists of a head into token order
+    // and turns scores into keys.  Inside the head lanes it is branch-free: every score
+    // is written, a rejected one into the lane's own pad slot, which is never read.
+    auto append_page = [&](const uint32_t (&sc)[4], int po) {
+        if (!head_lane) return;
+        const int t0 = (p_begin + po) * kPage + 4 * quad;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const uint64_t bi = __ballot((fm >> i) & 1u);
-            pre += (uint32_t)__popcll(bi & below);
-            tot += (uint32_t)__popcll(bi & colmask);
+            const bool take = (t0 + i < n) & (__uint_as_float(sc[i]) >= lo_f);
+            const uint32_t at = (take & (cnt < (uint32_t)kSubCap)) ? cnt : (uint32_t)kSubCap;
+            ck[my_list + at] = sc[i];
+            taken[(4 * po + i) >> 5] |= (take ? 1u : 0u) << ((4 * po + i) & 31);
+            cnt += take ? 1u : 0u;
         }
-        uint32_t pos = cnt + pre;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            if ((fm >> i) & 1u) {
-                if (pos < (uint32_t)kCandCap) {
-                    ck[col * kCandCap + pos] = key[i];
-                    cp[col * kCandCap + pos] = (uint16_t)(t0 + i - slot_tok0);
-                }
-                ++pos;
-            }
-        }
-        cnt += tot;
     };
-    auto score_group = [&](const u32x4 (&kr)[kScoreUnroll][4], int p) {
+    auto score_group = [&](u32x4 (&kr)[kScoreUnroll][4], int p, int p_next, bool reload) {
         stage_group(kr);
+        sched_fence();
+        if (reload) load_group(kr, p_next);
+        sched_fence();
+        // the operands of every staged page first: LDS operations complete in order, so
+        // an operand read issued after an append's writes would wait for them
+        bf16x8 op[kScoreUnroll][4];
+#pragma unroll
+        for (int u = 0; u < kScoreUnroll; ++u) read_operands(u, op[u]);
+        sched_fence();
 #pragma unroll
         for (int u = 0; u < kScoreUnroll; ++u) {
             if (p + u < p_end) {                              // wave-uniform
-                uint32_t key[4];
-                page_keys(u, key);
-                append_page(key, p + u);
+                uint32_t sc[4];
+                mfma_scores(op[u], sc);
+                append_page(sc, p - p_begin + u);
             }
         }
+        sched_fence();
     };
-    // the sample: keys of the wave's first pages kept, their top 16 bits to LDS
+    // the sample: scores of the wave's first pages kept, their keys' top 16 bits to LDS
     // (0 for tokens past the row)
     uint32_t skey[kSamplePagesPerWave][4];
-    auto sample_group = [&](const u32x4 (&kr)[kScoreUnroll][4], int su0) {
-        if (has_pages) stage_group(kr);
+    auto sample_group = [&](u32x4 (&kr)[kScoreUnroll][4], int su0) {
+        stage_group(kr);                                      // (a wave without pages stages
+        sched_fence();                                        //  and loads its row's last page)
+        load_group(kr, p_begin + su0 + 2 * kScoreUnroll);
+        sched_fence();
 #pragma unroll
         for (int u = 0; u < kScoreUnroll; ++u) {
             const int su = su0 + u, pp = p_begin + su;
-            uint32_t key[4] = {0u, 0u, 0u, 0u};
-            if (pp < p_end) page_keys(u, key);                // wave-uniform
+            uint32_t sc[4] = {0u, 0u, 0u, 0u};
+            if (pp < p_end) page_scores(u, sc);               // wave-uniform
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                skey[su][i] = key[i];
+                skey[su][i] = sc[i];
                 const int t = pp * kPage + 4 * quad + i;
                 if (head_lane)
                     samp[col][(wave * kSamplePagesPerWave + su) * kPage + 4 * quad + i] =
-                        (pp < p_end && t < n) ? (uint16_t)(key[i] >> 16) : (uint16_t)0;
+                        (pp < p_end && t < n) ? (uint16_t)(score_key(__uint_as_float(sc[i])) >> 16) : (uint16_t)0;
             }
         }
+        sched_fence();
     };
 
     // 1. the sample pages, with the next group's loads in flight
     u32x4 ka[kScoreUnroll][4], kb[kScoreUnroll][4];
-    if (has_pages) {
-        load_group(ka, p_begin);
-        load_group(kb, p_begin + kScoreUnroll);
+    load_group(ka, p_begin);                                  // unconditional: no control flow
+    sched_fence();                                            // around loads in flight
+    load_group(kb, p_begin + kScoreUnroll);
+    sched_fence();
+#pragma unroll
+    for (int gi = 0; gi < kSampleGroups; gi += 2) {
+        sample_group(ka, gi * kScoreUnroll);
+        sample_group(kb, (gi + 1) * kScoreUnroll);
     }
-    sample_group(ka, 0);
-    if (has_pages) load_group(ka, p_begin + 2 * kScoreUnroll);
-    sample_group(kb, kScoreUnroll);
-    if (has_pages) load_group(kb, p_begin + 3 * kScoreUnroll);
-    sample_group(ka, 2 * kScoreUnroll);
-    if (has_pages) load_group(ka, p_begin + 4 * kScoreUnroll);
-    sample_group(kb, 3 * kScoreUnroll);
-    if (has_pages) load_group(kb, p_begin + 5 * kScoreUnroll);
-    static_assert(kSamplePagesPerWave == 4 * kScoreUnroll, "the sample is four register groups");
-    __syncthreads();
-    // 2. wave hh: head hh's bound, the r-th largest sample code found by bisection,
+    lds_barrier();
+    // 2. per head hh (one wave each): its bound, the r-th largest sample code found by bisection,
     //    r = mu + 6 sqrt(mu) + 8 for mu the expected number of samples at or above
     //    the k-th key (a bound above the k-th key sends the row to the slow path, so
     //    the margin keeps that below about 1e-9 per workgroup and head)
-    if (wave < heads_here) {
+    for (int hh = wave; hh < heads_here; hh += kScoreWaves) {
         uint32_t b_lo = 0xFFFFFFFFu;                          // k' = 0 or N: no candidates needed
         if (kk > 0 && kk < n) {
             int s_valid = 0;
@@ -343,7 +376,7 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_kernel(
                 uint32_t c[per_lane];
 #pragma unroll
                 for (int v = 0; v < per_lane / 8; ++v) {
-                    const u32x4 w4 = *(const u32x4 *)&samp[wave][lane * per_lane + 8 * v];
+                    const u32x4 w4 = *(const u32x4 *)&samp[hh][lane * per_lane + 8 * v];
                     c[8 * v + 0] = w4.x & 0xFFFFu; c[8 * v + 1] = w4.x >> 16;
                     c[8 * v + 2] = w4.y & 0xFFFFu; c[8 * v + 3] = w4.y >> 16;
                     c[8 * v + 4] = w4.z & 0xFFFFu; c[8 * v + 5] = w4.z >> 16;
@@ -360,35 +393,75 @@ __global__ __launch_bounds__(kScoreWaves * 64) void score_kernel(
                 b_lo = lo_c << 16;
             }
         }
-        if (lane == 0) lo_lds[wave] = b_lo;
+        if (lane == 0) lo_lds[hh] = b_lo;
     }
-    __syncthreads();
+    lds_barrier();
     if (head_lane) lo = lo_lds[col];
+    // lo = 0: every score; ~0: none (the comparison with a NaN is false)
+    lo_f = lo == 0u ? -__builtin_inff() : __uint_as_float((lo & 0x80000000u) ? (lo & 0x7FFFFFFFu) : ~lo);
     // 3. the sample pages' candidates, then the rest of the stream
 #pragma unroll
     for (int su = 0; su < kSamplePagesPerWave; ++su)
-        if (p_begin + su < p_end) append_page(skey[su], p_begin + su);
+        if (p_begin + su < p_end) append_page(skey[su], su);
     if (has_pages) {                                          // wave-uniform
-        for (int p = p_begin + kSamplePagesPerWave; p < p_end; p += 2 * kScoreUnroll) {
-            score_group(ka, p);
-            load_group(ka, p + 2 * kScoreUnroll);
-            score_group(kb, p + kScoreUnroll);
-            load_group(kb, p + 3 * kScoreUnroll);
+        // fully unrolled: straight-line code lets the compiler wait for exactly the
+        // group it stages, with the next two groups still in flight
+        constexpr int kMainIters = (kScorePagesPerWave - kSamplePagesPerWave) / (2 * kScoreUnroll);
+#pragma unroll
+        for (int it = 0; it < kMainIters; ++it) {
+            const int o = kSamplePagesPerWave + it * 2 * kScoreUnroll;     // page offset in the wave
+            const int p = p_begin + o;
+            score_group(ka, p, p + 2 * kScoreUnroll, o + 2 * kScoreUnroll < kScorePagesPerWave);
+            score_group(kb, p + kScoreUnroll, p + 3 * kScoreUnroll, o + 3 * kScoreUnroll < kScorePagesPerWave);
         }
-        // this wave's slot: per head its count, bound and candidates in token order
+        // this wave's slot: per head its count, bound and candidates in token order.
+        // Head lane (col, quad) writes its own entries: the e-th set bit of its mask
+        // is the token of its e-th entry, which goes to e + (entries of the head's
+        // other lanes with a lower token).
         wave_lds_sync();
         const int slot = p_begin / kScorePagesPerWave;
-        for (int hh = 0; hh < heads_here; ++hh) {
-            const uint32_t c = (uint32_t)__shfl((int)cnt, hh, 64);   // lane hh is column hh
-            const int64_t row = ((int64_t)b * num_q_heads + h0 + hh) * slots + slot;
-            if (lane == 0) {
-                cand_cnt[row] = c > (uint32_t)kCandCap ? kCandOverflow : c;
-                cand_lo[row] = lo_lds[hh];
+        uint32_t oc[4], om[4][4], total = 0;
+        bool ovf = false;
+#pragma unroll
+        for (int q2 = 0; q2 < 4; ++q2) {
+            oc[q2] = (uint32_t)__shfl((int)cnt, col + 16 * q2, 64);
+#pragma unroll
+            for (int w = 0; w < 4; ++w) om[q2][w] = (uint32_t)__shfl((int)taken[w], col + 16 * q2, 64);
+            ovf |= oc[q2] > (uint32_t)kSubCap;
+            total += oc[q2];
+        }
+        if (head_lane) {
+            const int64_t row = ((int64_t)b * num_q_heads + h0 + col) * slots + slot;
+            if (quad == 0) {
+                cand_cnt[row] = ovf ? kCandOverflow : total;
+                cand_lo[row] = lo;
             }
-            if (c <= (uint32_t)kCandCap) {
-                for (int i = lane; i < (int)c; i += 64) {
-                    cand_key[row * kCandCap + i] = ck[hh * kCandCap + i];
-                    cand_pos[row * kCandCap + i] = cp[hh * kCandCap + i];
+            if (!ovf) {
+                uint32_t e = 0;
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    uint32_t bits = taken[w];
+                    while (bits) {
+                        const int j = 32 * w + __builtin_ctz(bits);   // 4 page + i
+                        bits &= bits - 1u;
+                        const int pg = j >> 2;
+                        uint32_t f = e;
+#pragma unroll
+                        for (int q2 = 0; q2 < 4; ++q2) {
+                            if (q2 == quad) continue;
+                            const int lim = 4 * pg + (q2 < quad ? 4 : 0);   // their bits below lim
+#pragma unroll
+                            for (int w2 = 0; w2 < 4; ++w2) {
+                                const int lo_bit = lim - 32 * w2;
+                                const uint32_t m = lo_bit >= 32 ? 0xFFFFFFFFu
+                                                 : lo_bit <= 0 ? 0u : ((1u << lo_bit) - 1u);
+                                f += (uint32_t)__popc(om[q2][w2] & m);
+                            }
+                        }
+                        cand_key[row * kCandCap + f] = score_key(__uint_as_float(ck[my_list + e]));
+                        cand_pos[row * kCandCap + f] = (uint16_t)(pg * kPage + 4 * quad + (j & 3));
+                        ++e;
+                    }
                 }
             }
         }
