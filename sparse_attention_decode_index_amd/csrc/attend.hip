@@ -9,13 +9,14 @@
 // 5.1) in fp32, split over chunks of the index list, and the chunk partials are
 // combined by merge_kernel with a log-sum-exp merge.
 //
-// Work decomposition: a workgroup of W waves (W = min(16, ceil(k_max / 64))) takes
-// 64 W consecutive entries of one (b, h) index row, 64 per wave, so rows with
-// k <= 1024 need no second launch.  Inside a wave, each group of 16 lanes owns one
-// gathered row at a time (16 lanes x 16 B = the 256 B row, one 128-bit load per
-// lane for K and one for V); 8 rows of a group are in flight at once, and each
-// group keeps its own running softmax state; the 4 groups, then the W waves, are
-// merged at the end.
+// Work decomposition: a workgroup of W waves takes 64 W consecutive entries of one
+// (b, h) index row, 64 per wave.  Rows of up to 1024 entries take one workgroup
+// (W = ceil(k_max / 64)) and need no second launch; longer rows are cut into chunks
+// of 4 waves whose partials merge_kernel combines.  Inside a wave, each group of 16
+// lanes owns one gathered row at a time (16 lanes x 16 B = the 256 B row, one
+// 128-bit load per lane for K and one for V); 8 (wide workgroups) or all 16 (chunks)
+// rows of a group are in flight at once, and each group keeps its own running
+// softmax state; the 4 groups, then the W waves, are merged at the end.
 #include "sdi_device.hpp"
 #include "sdi_launch.hpp"
 
@@ -23,21 +24,31 @@ namespace sdi {
 
 constexpr int kAttMaxWaves = 16;
 constexpr int kAttPerWave = 64;
-constexpr int kAttBatch = 8;                            // rows per 16-lane group in flight
+constexpr int kAttWideMax = kAttMaxWaves * kAttPerWave; // rows up to 1024 entries: one workgroup each
+constexpr int kAttChunkWaves = 4;                       // longer rows: 256-entry chunks + a merge
 
-int attend_waves(int k_max) { return std::min(kAttMaxWaves, (k_max + kAttPerWave - 1) / kAttPerWave); }
+// Rows of up to 1024 entries get one workgroup of ceil(k_max / 64) waves that writes
+// the output itself.  Longer (or ragged) rows are cut into 256-entry chunks of 4
+// waves: small workgroups keep a CU busy when a row's last chunk is short, and a
+// wave's 16 rows per lane group are all in flight at once.
+int attend_waves(int k_max)
+{
+    return k_max <= kAttWideMax ? (k_max + kAttPerWave - 1) / kAttPerWave : kAttChunkWaves;
+}
 constexpr float kLog2e = 1.4426950408889634f;
 
-// grid (splits, num_q_heads, batch); 64 W threads.
-__global__ __launch_bounds__(kAttMaxWaves * 64) void attend_kernel(
+// grid (splits, num_q_heads, batch); 64 W threads, W <= MAXW; BATCH rows per 16-lane
+// group are loaded at once (16 = all of them).
+template <int MAXW, int BATCH>
+__global__ __launch_bounds__(MAXW * 64) void attend_kernel(
     const uint16_t *__restrict__ kc, const uint16_t *__restrict__ vc, const int32_t *__restrict__ page_table,
     const int32_t *__restrict__ seq_lens, const uint16_t *__restrict__ q, const int32_t *__restrict__ idx,
     const int32_t *__restrict__ k_per_seq, int num_q_heads, int num_kv_heads, int group, int max_pages, int k_max,
     float scale_log2, int splits, float *__restrict__ part_ml, float *__restrict__ part_acc,
     float *__restrict__ out)
 {
-    __shared__ float red_acc[kAttMaxWaves][kHeadDim];
-    __shared__ float red_ml[kAttMaxWaves][2];
+    __shared__ float red_acc[MAXW][kHeadDim];
+    __shared__ float red_ml[MAXW][2];
     const int waves = blockDim.x >> 6;
     const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int64_t bh = (int64_t)b * num_q_heads + h;
@@ -80,11 +91,11 @@ __global__ __launch_bounds__(kAttMaxWaves * 64) void attend_kernel(
     for (int d = 0; d < 8; ++d) acc[d] = 0.f;
 
 #pragma unroll
-    for (int r0 = 0; r0 < kAttPerWave / 4; r0 += kAttBatch) {
-        u32x4 kw[kAttBatch], vw[kAttBatch];
-        int rows[kAttBatch];
+    for (int r0 = 0; r0 < kAttPerWave / 4; r0 += BATCH) {
+        u32x4 kw[BATCH], vw[BATCH];
+        int rows[BATCH];
 #pragma unroll
-        for (int r = 0; r < kAttBatch; ++r) {
+        for (int r = 0; r < BATCH; ++r) {
             rows[r] = __shfl(my_row, (r0 + r) * 4 + grp, 64);
             kw[r] = u32x4{0u, 0u, 0u, 0u};
             vw[r] = u32x4{0u, 0u, 0u, 0u};
@@ -94,10 +105,10 @@ __global__ __launch_bounds__(kAttMaxWaves * 64) void attend_kernel(
                 vw[r] = __builtin_nontemporal_load((const u32x4 *)(vc + off));
             }
         }
-        float x[kAttBatch];
+        float x[BATCH];
         float bmax = -INFINITY;
 #pragma unroll
-        for (int r = 0; r < kAttBatch; ++r) {
+        for (int r = 0; r < BATCH; ++r) {
             float kf[8];
             unpack8(kw[r], kf);
             float s = 0.f;
@@ -114,7 +125,7 @@ __global__ __launch_bounds__(kAttMaxWaves * 64) void attend_kernel(
 #pragma unroll
             for (int d = 0; d < 8; ++d) acc[d] *= alpha;
 #pragma unroll
-            for (int r = 0; r < kAttBatch; ++r) {
+            for (int r = 0; r < BATCH; ++r) {
                 const float p = fast_exp2(x[r] - m_new);
                 float vf[8];
                 unpack8(vw[r], vf);
@@ -265,10 +276,17 @@ hipError_t launch_attend(const AttendArgs &a, hipStream_t stream)
     float *part_acc = (float *)a.ws;
     float *part_ml = splits > 1 ? part_acc + bhs * kHeadDim : nullptr;
     const int waves = attend_waves(a.k_max);
-    hipLaunchKernelGGL(attend_kernel, dim3(splits, a.num_q_heads, a.batch), dim3(waves * 64), 0, stream,
-                       (const uint16_t *)a.k_cache, (const uint16_t *)a.v_cache, a.page_table, a.seq_lens,
-                       (const uint16_t *)a.q, a.idx, a.k_per_seq, a.num_q_heads, a.num_kv_heads, group, a.max_pages,
-                       a.k_max, a.scale * kLog2e, splits, part_ml, part_acc, a.out);
+    const dim3 grid(splits, a.num_q_heads, a.batch);
+    if (a.k_max <= kAttWideMax)
+        hipLaunchKernelGGL((attend_kernel<kAttMaxWaves, 8>), grid, dim3(waves * 64), 0, stream,
+                           (const uint16_t *)a.k_cache, (const uint16_t *)a.v_cache, a.page_table, a.seq_lens,
+                           (const uint16_t *)a.q, a.idx, a.k_per_seq, a.num_q_heads, a.num_kv_heads, group,
+                           a.max_pages, a.k_max, a.scale * kLog2e, splits, part_ml, part_acc, a.out);
+    else
+        hipLaunchKernelGGL((attend_kernel<kAttChunkWaves, 16>), grid, dim3(waves * 64), 0, stream,
+                           (const uint16_t *)a.k_cache, (const uint16_t *)a.v_cache, a.page_table, a.seq_lens,
+                           (const uint16_t *)a.q, a.idx, a.k_per_seq, a.num_q_heads, a.num_kv_heads, group,
+                           a.max_pages, a.k_max, a.scale * kLog2e, splits, part_ml, part_acc, a.out);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || splits == 1) return e;
     return launch_merge(part_ml, part_acc, splits, waves * kAttPerWave, a.k_per_seq, a.k_max, a.batch,

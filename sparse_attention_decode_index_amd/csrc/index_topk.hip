@@ -53,8 +53,8 @@ constexpr int kWaveTokens = kScorePagesPerWave * kPage;       // 512 tokens: one
 constexpr int kScoreTokensPerBlock = kScoreWaves * kWaveTokens;
 constexpr int kStageRow = kRowBytes + 16;                     // padded LDS row: conflict-free both ways
 constexpr int kStagePage = kPage * kStageRow;                 // 4352 B
-constexpr int kCandCap = 128;                                 // candidates kept per (slot, head)
-constexpr int kSubCap = kCandCap / 4;                         // ... as 4 lane lists (one per quad) of 32
+constexpr int kCandCap = 192;                                 // candidates kept per (slot, head)
+constexpr int kSubCap = kCandCap / 4;                         // ... as 4 lane lists (one per quad) of 48
 constexpr int kSubStride = kSubCap + 1;                       // padded: lists start in different banks
 constexpr uint32_t kCandOverflow = 0xFFFFFFFFu;               // slot count of an overflowed list
 constexpr int kSamplePagesPerWave = 16;                       // the first pages of each wave ...
@@ -641,7 +641,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a)
     if (threadIdx.x < 8) res[threadIdx.x] = threadIdx.x == 5 ? 0xFFFFFFFFu : 0u;
     if (!generic) {
         // 1. slot counts -> each candidate's place; slot i writes the workspace offsets of
-        //    its entries (i * 128 + j) at their places in ctok, the gather map.  An
+        //    its entries (i * kCandCap + j) at their places in ctok, the gather map.  An
         //    overflowed slot sends the row to the generic path.
         const uint32_t *cnt_row = a.cand_cnt + bh * a.slots, *lo_row = a.cand_lo + bh * a.slots;
         int bad = 0;
@@ -660,7 +660,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a)
             uint32_t tot;
             const uint32_t p0 = total + block_exclusive_scan<kSelThreads>(c, scratch, tot);
             for (uint32_t j = 0; j < c; ++j)
-                if (p0 + j < (uint32_t)a.cap) ctok[p0 + j] = ((uint32_t)i << 7) | j;
+                if (p0 + j < (uint32_t)a.cap) ctok[p0 + j] = (uint32_t)i * kCandCap + j;
             total += tot;
         }
         generic = bad != 0 || total < (uint32_t)kk || total > (uint32_t)a.cap;
@@ -703,7 +703,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a)
             const uint32_t v = v0 + u * kSelThreads + threadIdx.x;
             if (v < total) {
                 ckey[v] = kv[u];
-                ctok[v] = (av[u] >> 7) * kWaveTokens + tv[u];
+                ctok[v] = (av[u] / kCandCap) * kWaveTokens + tv[u];
                 dor |= kv[u] - lo;
             }
         }
