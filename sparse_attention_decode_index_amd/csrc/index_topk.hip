@@ -40,6 +40,7 @@
 #include "sdi_launch.hpp"
 
 #include <atomic>
+#include <cmath>
 
 namespace sdi {
 
@@ -191,7 +192,7 @@ __global__ __launch_bounds__(kScoreWaves * 64, 2) void score_kernel(
     const int32_t *__restrict__ seq_lens, const uint16_t *__restrict__ q, const int32_t *__restrict__ k_per_seq,
     int num_q_heads, int num_kv_heads, int group, int head_blocks, int max_pages, int k_max,
     uint32_t *__restrict__ cand_key, uint16_t *__restrict__ cand_pos, uint32_t *__restrict__ cand_cnt,
-    uint32_t *__restrict__ cand_lo, int slots)
+    uint32_t *__restrict__ cand_lo, uint32_t *__restrict__ cand_hi, int slots)
 {
     __shared__ int32_t pt_lds[kScoreWaves * kScorePagesPerWave];
     __shared__ __attribute__((aligned(16))) unsigned char stage_all[kScoreWaves * kScoreUnroll * kStagePage];
@@ -430,8 +431,9 @@ __global__ __launch_bounds__(kScoreWaves * 64, 2) void score_kernel(
             ovf |= oc[q2] > (uint32_t)kSubCap;
             total += oc[q2];
         }
+        const int64_t row = ((int64_t)b * num_q_heads + h0 + col) * slots + slot;
+        uint32_t kmax = 0;                                    // largest key this lane writes
         if (head_lane) {
-            const int64_t row = ((int64_t)b * num_q_heads + h0 + col) * slots + slot;
             if (quad == 0) {
                 cand_cnt[row] = ovf ? kCandOverflow : total;
                 cand_lo[row] = lo;
@@ -458,13 +460,20 @@ __global__ __launch_bounds__(kScoreWaves * 64, 2) void score_kernel(
                                 f += (uint32_t)__popc(om[q2][w2] & m);
                             }
                         }
-                        cand_key[row * kCandCap + f] = score_key(__uint_as_float(ck[my_list + e]));
+                        const uint32_t key = score_key(__uint_as_float(ck[my_list + e]));
+                        kmax = max(kmax, key);
+                        cand_key[row * kCandCap + f] = key;
                         cand_pos[row * kCandCap + f] = (uint16_t)(pg * kPage + 4 * quad + (j & 3));
                         ++e;
                     }
                 }
             }
         }
+        // the slot's largest candidate key (bounds the select's radix digits)
+        uint32_t hm = 0;
+#pragma unroll
+        for (int q2 = 0; q2 < 4; ++q2) hm = max(hm, (uint32_t)__shfl((int)kmax, col + 16 * q2, 64));
+        if (head_lane && quad == 0) cand_hi[row] = hm;
     }
 }
 
@@ -498,36 +507,45 @@ struct LdsCandidates {
     __device__ int32_t token(int pos) const { return (int32_t)tok[pos]; }
 };
 
+template <class Src>
+__device__ __forceinline__ void compact_selected(const Src &src, int n, int kk, int k_max, uint32_t T, uint32_t r,
+                                                 uint32_t *scratch, int32_t *__restrict__ out);
+
 // Exact selection over n keys in token order, every key >= base: radix passes over
 // the digits of d = key - base (d < 2^bits), 12 bits at a time from the top, find
 // the kk-th largest key T and how many keys equal to T to take (the first ones,
 // i.e. the lowest tokens); one ordered-compaction pass then writes the selected
 // tokens ascending and pads the row with -1.  Returns false, writing nothing, if
-// T < min_t.
+// T < min_t.  With first_hist_ready the caller has already counted the first digit
+// into hist (and zeroed res[0..1]).
 template <class Src>
 __device__ __forceinline__ bool radix_select(const Src &src, int n, int kk, int k_max, uint32_t base, int bits,
                                              uint32_t min_t, uint32_t *hist, uint32_t *scratch, uint32_t *res,
-                                             int32_t *__restrict__ out)
+                                             int32_t *__restrict__ out, bool first_hist_ready = false)
 {
     uint32_t prefix = 0, need = (uint32_t)kk;
     int hi = bits;                                           // digits above bit hi are fixed (= prefix)
+    bool ready = first_hist_ready;                           // the caller built the first digit's histogram
 #pragma unroll 1
     while (hi > 0) {
         const int w = min(12, hi), lo = hi - w, nb = max(64, 1 << w);
-        for (int i = threadIdx.x; i < nb; i += kSelThreads) hist[i] = 0u;
-        if (threadIdx.x == 0) { res[0] = 0u; res[1] = 0u; }
-        __syncthreads();
-        for (int i0 = 0; i0 < n; i0 += kSelTile) {
-            uint32_t v[8];
-            const int cnt = src.load8(i0 + threadIdx.x * kSelPerThread, n, v);
+        if (!ready) {
+            for (int i = threadIdx.x; i < nb; i += kSelThreads) hist[i] = 0u;
+            if (threadIdx.x == 0) { res[0] = 0u; res[1] = 0u; }
+            __syncthreads();
+            for (int i0 = 0; i0 < n; i0 += kSelTile) {
+                uint32_t v[8];
+                const int cnt = src.load8(i0 + threadIdx.x * kSelPerThread, n, v);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const uint32_t d = v[e] - base;
-                if (e < cnt && (hi == 32 || (d >> hi) == prefix))
-                    atomicAdd(&hist[(d >> lo) & ((1u << w) - 1u)], 1u);
+                for (int e = 0; e < 8; ++e) {
+                    const uint32_t d = v[e] - base;
+                    if (e < cnt && (hi == 32 || (d >> hi) == prefix))
+                        atomicAdd(&hist[(d >> lo) & ((1u << w) - 1u)], 1u);
+                }
             }
+            __syncthreads();
         }
-        __syncthreads();
+        ready = false;
         threshold_bin_wave(hist, nb, need, res);
         need -= res[1];
         prefix = (prefix << w) | res[0];
@@ -537,6 +555,16 @@ __device__ __forceinline__ bool radix_select(const Src &src, int n, int kk, int 
     prefix += base;
     const uint32_t T = prefix, r = need;                     // take keys > T and the first r keys == T
     if (T < min_t) return false;
+    compact_selected(src, n, kk, k_max, T, r, scratch, out);
+    return true;
+}
+
+// Ordered compaction: writes, in token order, the keys > T and the first r keys == T
+// (at most kk tokens), then pads the row to k_max with -1.
+template <class Src>
+__device__ __forceinline__ void compact_selected(const Src &src, int n, int kk, int k_max, uint32_t T, uint32_t r,
+                                                 uint32_t *scratch, int32_t *__restrict__ out)
+{
     uint32_t run_sel = 0, run_eq = 0;
     for (int base = 0; base < n; base += kSelTile) {
         uint32_t v[8];
@@ -568,7 +596,6 @@ __device__ __forceinline__ bool radix_select(const Src &src, int n, int kk, int 
         run_eq += tot >> 16;
     }
     for (int i = (int)run_sel + threadIdx.x; i < k_max; i += kSelThreads) out[i] = -1;
-    return true;
 }
 
 struct SelectArgs {
@@ -579,6 +606,7 @@ struct SelectArgs {
     const uint16_t *cand_pos;                                 // token - 512 slot, same layout
     const uint32_t *cand_cnt;                                 // [row][slot]
     const uint32_t *cand_lo;                                  // [row][slot]: the slot's bound
+    const uint32_t *cand_hi;                                  // [row][slot]: its largest candidate key
     int slots;                                                // slots per row
     int cap;                                                  // candidates the LDS holds (0: generic only)
     uint32_t *keys32;                                         // generic-path scratch, one row per (b, h)
@@ -623,6 +651,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a)
     __shared__ __attribute__((aligned(16))) uint32_t hist[kHistBins];
     __shared__ uint32_t scratch[kSelWaves + 2];
     __shared__ uint32_t res[8];
+    __shared__ uint32_t blist[64];                            // keys of the threshold bin
 
     const int h = blockIdx.x, b = blockIdx.y;
     const int64_t bh = (int64_t)b * a.num_q_heads + h;
@@ -644,15 +673,21 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a)
         //    its entries (i * kCandCap + j) at their places in ctok, the gather map.  An
         //    overflowed slot sends the row to the generic path.
         const uint32_t *cnt_row = a.cand_cnt + bh * a.slots, *lo_row = a.cand_lo + bh * a.slots;
+        const uint32_t *hi_row = a.cand_hi + bh * a.slots;
         int bad = 0;
-        uint32_t lo_min = 0xFFFFFFFFu, lo_max = 0u;
-        for (int base = 0; base < nslots; base += kSelThreads) {
+        uint32_t lo_min = 0xFFFFFFFFu, lo_max = 0u, hi_max = 0u;
+        for (int i = threadIdx.x; i < kHistBins; i += kSelThreads) hist[i] = 0u;
+        for (int base = 0; base < a.slots; base += kSelThreads) {
+            // loaded for every allocated slot (no wait for seq_lens), used below nslots
             const int i = base + (int)threadIdx.x;
-            uint32_t c = i < nslots ? cnt_row[i] : 0u;
+            const bool in_ws = i < a.slots;
+            const uint32_t c_raw = in_ws ? cnt_row[i] : 0u, l = in_ws ? lo_row[i] : 0u;
+            const uint32_t hv = in_ws ? hi_row[i] : 0u;
+            uint32_t c = i < nslots ? c_raw : 0u;
             if (i < nslots) {
-                const uint32_t l = lo_row[i];
                 lo_min = min(lo_min, l);
                 lo_max = max(lo_max, l);
+                if (c != 0u && c != kCandOverflow) hi_max = max(hi_max, hv);
             }
             const bool ovf = c == kCandOverflow;
             c = ovf ? 0u : c;
@@ -668,24 +703,28 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a)
         for (int m = 32; m >= 1; m >>= 1) {
             lo_min = min(lo_min, (uint32_t)__shfl_xor((int)lo_min, m, 64));
             lo_max = max(lo_max, (uint32_t)__shfl_xor((int)lo_max, m, 64));
+            hi_max = max(hi_max, (uint32_t)__shfl_xor((int)hi_max, m, 64));
         }
         if ((threadIdx.x & 63) == 0) {
             atomicMin(&res[5], lo_min);
             atomicMax(&res[6], lo_max);
+            atomicMax(&res[7], hi_max);
         }
-        __syncthreads();                                      // map and bounds complete
+        __syncthreads();                                      // map, bounds and cleared histogram complete
     }
     if (generic) {
         select_rescore_generic(a, bh, b, h, n, kk, hist, scratch, res, out);
         return;
     }
     // 2. gather the candidates into LDS, in token order (4 loads per thread in flight),
-    //    and the OR of key - lo, lo the smallest bound, whose bit length bounds the
-    //    radix digits
+    //    counting the first radix digit of d = key - lo on the way: lo is the smallest
+    //    bound, and the largest candidate key gives the digits' span (bits)
     const uint32_t lo = res[5], lo_max = res[6];
+    const int bits = 32 - __clz((int)(res[7] - lo));
+    const int w0 = min(12, bits), sh0 = bits - w0;
+    const uint32_t mask0 = (1u << w0) - 1u;
     const uint32_t *key_row = a.cand_key + bh * a.slots * kCandCap;
     const uint16_t *pos_row = a.cand_pos + bh * a.slots * kCandCap;
-    uint32_t dor = 0;
     for (uint32_t v0 = 0; v0 < total; v0 += 4 * kSelThreads) {
         uint32_t av[4], kv[4], tv[4];
 #pragma unroll
@@ -704,19 +743,65 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a)
             if (v < total) {
                 ckey[v] = kv[u];
                 ctok[v] = (av[u] / kCandCap) * kWaveTokens + tv[u];
-                dor |= kv[u] - lo;
+                if (bits > 0) atomicAdd(&hist[((kv[u] - lo) >> sh0) & mask0], 1u);
             }
         }
     }
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) dor |= (uint32_t)__shfl_xor((int)dor, m, 64);
-    if ((threadIdx.x & 63) == 0 && dor) atomicOr(&res[7], dor);
+    if (threadIdx.x == 0) { res[0] = 0u; res[1] = 0u; res[2] = 0u; }
     __syncthreads();
-    const int bits = 32 - __clz((int)res[7]);
-    // 3. exact selection among the candidates, valid if the k-th key reaches every bound
-    if (!radix_select(LdsCandidates{ckey, ctok}, (int)total, kk, a.k_max, lo, bits, lo_max, hist, scratch, res,
-                      out))
+    // 3. the k-th key T and r, the number of keys equal to T to take (the first ones):
+    //    the first digit's bin b0 holds it; if the whole bin is taken and its floor
+    //    already reaches every bound, the bin floor is T with all ties; otherwise the
+    //    bin's few entries are ranked exactly by one wave.  The selection is valid if T
+    //    reaches every workgroup bound.
+    const LdsCandidates cands{ckey, ctok};
+    uint32_t T = lo, r = (uint32_t)kk;
+    if (bits > 0) {
+        threshold_bin_wave(hist, max(64, 1 << w0), (uint32_t)kk, res);
+        const uint32_t b0 = res[0], need0 = (uint32_t)kk - res[1], floor0 = lo + (b0 << sh0);
+        if (need0 == hist[b0] && floor0 >= lo_max) {
+            T = floor0;
+            r = 0xFFFFFFFFu;
+        } else {
+            for (uint32_t v = threadIdx.x; v < total; v += kSelThreads) {
+                const uint32_t key = ckey[v];
+                if (((key - lo) >> sh0) == b0) {
+                    const uint32_t at = atomicAdd(&res[2], 1u);
+                    if (at < 64u) blist[at] = key;
+                }
+            }
+            __syncthreads();
+            const uint32_t m = res[2];
+            if (m > 64u) {                                    // a crowded bin: full radix passes
+                __syncthreads();
+                if (!radix_select(cands, (int)total, kk, a.k_max, lo, bits, lo_max, hist, scratch, res, out))
+                    select_rescore_generic(a, bh, b, h, n, kk, hist, scratch, res, out);
+                return;
+            }
+            if (threadIdx.x < 64) {                           // need0-th largest of the bin, by rank
+                const int lane = threadIdx.x;
+                const uint32_t mine = lane < (int)m ? blist[lane] : 0u;
+                uint32_t gt = 0, eq = 0;
+                for (uint32_t j = 0; j < m; ++j) {
+                    const uint32_t o = blist[j];
+                    gt += o > mine ? 1u : 0u;
+                    eq += o == mine ? 1u : 0u;
+                }
+                const uint64_t hit = __ballot(lane < (int)m && gt < need0 && need0 <= gt + eq);
+                const int L = __ffsll((unsigned long long)hit) - 1;
+                if (lane == L) { res[3] = mine; res[4] = need0 - gt; }
+            }
+            __syncthreads();
+            T = res[3];
+            r = res[4];
+        }
+    }
+    if (T < lo_max) {                                         // some workgroup's bound lies above T
+        __syncthreads();
         select_rescore_generic(a, bh, b, h, n, kk, hist, scratch, res, out);
+        return;
+    }
+    compact_selected(cands, (int)total, kk, a.k_max, T, r, scratch, out);
 }
 
 // ---- host side ---------------------------------------------------------------------------
@@ -728,10 +813,11 @@ static int index_topk_slots(int n_max) { return (n_max + kWaveTokens - 1) / kWav
 size_t index_topk_workspace_bytes(int batch, int num_q_heads, int n_max)
 {
     // per (b, h): a 32-bit key row for the generic path, then per 512-token slot the
-    // candidate list (32-bit keys, 16-bit positions), its count and its bound
+    // candidate list (32-bit keys, 16-bit positions), its count, its bound and its
+    // largest key
     const size_t rows = (size_t)batch * num_q_heads, slots = (size_t)index_topk_slots(n_max);
     return rows * (index_topk_key_stride(n_max) * sizeof(uint32_t) +
-                   slots * (kCandCap * (sizeof(uint32_t) + sizeof(uint16_t)) + 2 * sizeof(uint32_t)));
+                   slots * (kCandCap * (sizeof(uint32_t) + sizeof(uint16_t)) + 3 * sizeof(uint32_t)));
 }
 
 hipError_t launch_index_topk(const IndexArgs &a, hipStream_t stream)
@@ -745,16 +831,22 @@ hipError_t launch_index_topk(const IndexArgs &a, hipStream_t stream)
     uint32_t *cand_key = keys32 + rows * stride;
     uint32_t *cand_cnt = cand_key + rows * slots * kCandCap;
     uint32_t *cand_lo = cand_cnt + rows * slots;
-    uint16_t *cand_pos = (uint16_t *)(cand_lo + rows * slots);
+    uint32_t *cand_hi = cand_lo + rows * slots;
+    uint16_t *cand_pos = (uint16_t *)(cand_hi + rows * slots);
 
     dim3 sgrid((a.n_max + kScoreTokensPerBlock - 1) / kScoreTokensPerBlock, a.num_kv_heads * head_blocks, a.batch);
     hipLaunchKernelGGL(score_kernel, sgrid, dim3(kScoreWaves * 64), 0, stream, (const uint16_t *)a.k_cache,
                        a.page_table, a.seq_lens, (const uint16_t *)a.q, a.k_per_seq, a.num_q_heads,
                        a.num_kv_heads, group, head_blocks, a.max_pages, a.k_max, cand_key, cand_pos, cand_cnt,
-                       cand_lo, slots);
+                       cand_lo, cand_hi, slots);
 
-    // LDS for the candidates: three per selected token plus slack, within the budget
-    const int cap = (int)std::min<int64_t>(kSelCapMax, 3 * (int64_t)a.k_max + 1024);
+    // LDS for the candidates.  A workgroup's bound is reached by about (n_w / 1024) r
+    // of its n_w tokens, r = mu + 6 sqrt(mu) + 8 and mu = 1024 k / n, so a row has
+    // about k + 6 sqrt(k n / 1024) + 8 n / 1024 candidates; the largest row bounds it
+    // (15% margin).  Rows beyond the capacity take the re-scoring path.
+    const double kd = a.k_max, nd = a.n_max;
+    const double expect = kd + 6.0 * std::sqrt(kd * nd / 1024.0) + 8.0 * nd / 1024.0;
+    const int cap = (int)std::min<double>(kSelCapMax, std::ceil(1.15 * expect) + 256.0);
     const size_t dyn = (size_t)cap * 2 * sizeof(uint32_t);
     if (dyn > 64 * 1024) {
         // raise the kernel's dynamic-LDS limit to the budget once (a function attribute,
@@ -768,7 +860,7 @@ hipError_t launch_index_topk(const IndexArgs &a, hipStream_t stream)
         }
     }
     SelectArgs s{(const uint16_t *)a.k_cache, a.page_table, a.seq_lens, a.k_per_seq, (const uint16_t *)a.q,
-                 cand_key, cand_pos, cand_cnt, cand_lo, slots, cap, keys32, stride, a.num_q_heads, a.num_kv_heads,
+                 cand_key, cand_pos, cand_cnt, cand_lo, cand_hi, slots, cap, keys32, stride, a.num_q_heads, a.num_kv_heads,
                  group, a.max_pages, a.k_max, a.idx_out};
     hipLaunchKernelGGL(select_kernel, dim3(a.num_q_heads, a.batch), dim3(kSelThreads), dyn, stream, s);
     return hipGetLastError();

@@ -53,8 +53,8 @@ def test_workspace_sizes(lib):
     k = kv()
     n1 = lib.sparse_decode_index_topk_workspace(ctypes.byref(k), 8, 5)
     # per row: a 32-bit key row (padded to 128 tokens), then per 512-token slot 192 candidates
-    # (32-bit key + 16-bit position), a count and the slot's lower bound
-    assert n1 == 2 * 8 * (256 * 4 + 1 * (192 * 6 + 8))
+    # (32-bit key + 16-bit position), a count, the slot's lower bound and its largest key
+    assert n1 == 2 * 8 * (256 * 4 + 1 * (192 * 6 + 12))
     assert lib.sparse_decode_attend_workspace(ctypes.byref(k), 8, 1024) == 0         # one chunk: no partials
     assert lib.sparse_decode_attend_workspace(ctypes.byref(k), 8, 1025) == 2 * 8 * 5 * 130 * 4   # 256-entry chunks
     assert lib.dense_decode_workspace(ctypes.byref(k), 8) == 2 * 8 * 1 * 130 * 4      # one 1024-token chunk
