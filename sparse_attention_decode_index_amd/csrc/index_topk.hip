@@ -58,6 +58,12 @@ constexpr int kCandCap = 192;                                 // candidates kept
 constexpr int kSubCap = kCandCap / 4;                         // ... as 4 lane lists (one per quad) of 48
 constexpr int kSubStride = kSubCap + 1;                       // padded: lists start in different banks
 constexpr uint32_t kCandOverflow = 0xFFFFFFFFu;               // slot count of an overflowed list
+// A slot's record for one head, 1280 B (ten 128-byte lines): 32-bit keys [0, 192),
+// then the tail: count, bound, largest key, 0, and the 16-bit positions (token - slot
+// start) in token order.
+constexpr int kRecTailWords = 128;                            // 512 B: 4 header words + 192 positions
+constexpr int kRecWords = kCandCap + kRecTailWords;
+static_assert(4 + kCandCap / 2 <= kRecTailWords && kRecWords * 4 % 128 == 0, "record layout");
 constexpr int kSamplePagesPerWave = 16;                       // the first pages of each wave ...
 constexpr int kBlockSample = kScoreWaves * kSamplePagesPerWave * kPage;   // ... 1024 tokens per head
 constexpr int kSampleGroups = kSamplePagesPerWave / kScoreUnroll;
@@ -70,7 +76,7 @@ constexpr int kSelWaves = kSelThreads / 64;
 constexpr int kSelPerThread = 8;
 constexpr int kSelTile = kSelThreads * kSelPerThread;
 constexpr int kSelCapMax = 16384;                             // candidates gathered into LDS
-constexpr int kSelDynMax = kSelCapMax * 8;                    // dynamic LDS: candidate keys + tokens
+constexpr int kSelDynMax = 96 * 1024;                         // dynamic LDS: candidate keys + slot starts
 
 // MFMA B operand for the q rows of a head block: lane (col, quad) holds head col's
 // dims 32 s + 8 quad .. +7 (zeros for heads past the block).
@@ -191,8 +197,7 @@ __global__ __launch_bounds__(kScoreWaves * 64, 2) void score_kernel(
     const uint16_t *__restrict__ kc, const int32_t *__restrict__ page_table,
     const int32_t *__restrict__ seq_lens, const uint16_t *__restrict__ q, const int32_t *__restrict__ k_per_seq,
     int num_q_heads, int num_kv_heads, int group, int head_blocks, int max_pages, int k_max,
-    uint32_t *__restrict__ cand_key, uint16_t *__restrict__ cand_pos, uint32_t *__restrict__ cand_cnt,
-    uint32_t *__restrict__ cand_lo, uint32_t *__restrict__ cand_hi, int slots)
+    uint32_t *__restrict__ cand_rec, int slots)
 {
     __shared__ int32_t pt_lds[kScoreWaves * kScorePagesPerWave];
     __shared__ __attribute__((aligned(16))) unsigned char stage_all[kScoreWaves * kScoreUnroll * kStagePage];
@@ -415,10 +420,18 @@ __global__ __launch_bounds__(kScoreWaves * 64, 2) void score_kernel(
             score_group(ka, p, p + 2 * kScoreUnroll, o + 2 * kScoreUnroll < kScorePagesPerWave);
             score_group(kb, p + kScoreUnroll, p + 3 * kScoreUnroll, o + 3 * kScoreUnroll < kScorePagesPerWave);
         }
-        // this wave's slot: per head its count, bound and candidates in token order.
-        // Head lane (col, quad) writes its own entries: the e-th set bit of its mask
-        // is the token of its e-th entry, which goes to e + (entries of the head's
-        // other lanes with a lower token).
+        // this wave's slot: per head one record (count, bound, largest key, then the
+        // candidates in token order).  Head lane (col, quad) places its own entries:
+        // the e-th set bit of its mask is the token of its e-th entry, which goes to
+        // e + (entries of the head's other lanes with a lower token).  The records are
+        // assembled in LDS (the stage tile takes the keys, this wave's quarter of the
+        // sample codes the header and positions, both free now) and leave in whole
+        // 128-byte lines: a partial line costs HBM a read-modify-write, and these
+        // writes share the memory with the key stream.
+        uint32_t *out_key = (uint32_t *)stage;                                 // [head][kCandCap]
+        uint32_t *out_tail = (uint32_t *)(&samp[0][0] + wave * (kHeadBlock * kBlockSample / kScoreWaves));
+        static_assert(kHeadBlock * kCandCap * 4 <= kScoreUnroll * kStagePage, "keys fit the stage tile");
+        static_assert(kHeadBlock * kRecTailWords * 4 <= kHeadBlock * kBlockSample * 2 / kScoreWaves, "tails fit");
         wave_lds_sync();
         const int slot = p_begin / kScorePagesPerWave;
         uint32_t oc[4], om[4][4], total = 0;
@@ -431,41 +444,41 @@ __global__ __launch_bounds__(kScoreWaves * 64, 2) void score_kernel(
             ovf |= oc[q2] > (uint32_t)kSubCap;
             total += oc[q2];
         }
-        const int64_t row = ((int64_t)b * num_q_heads + h0 + col) * slots + slot;
-        uint32_t kmax = 0;                                    // largest key this lane writes
-        if (head_lane) {
-            if (quad == 0) {
-                cand_cnt[row] = ovf ? kCandOverflow : total;
-                cand_lo[row] = lo;
+        uint32_t *tail = out_tail + min(col, kHeadBlock - 1) * kRecTailWords;
+        uint16_t *tail_pos = (uint16_t *)(tail + 4);
+        uint32_t kmax = 0;                                    // largest key this lane places
+        if (head_lane && !ovf) {
+            // the other lanes' entries in the mask words before word w (a prefix of
+            // whole-word counts); inside word w only the partial word is counted
+            uint32_t before_word[4], run = 0;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                before_word[w] = run;
+#pragma unroll
+                for (int q2 = 0; q2 < 4; ++q2) run += q2 == quad ? 0u : (uint32_t)__popc(om[q2][w]);
             }
-            if (!ovf) {
-                uint32_t e = 0;
+            uint32_t e = 0;
 #pragma unroll
-                for (int w = 0; w < 4; ++w) {
-                    uint32_t bits = taken[w];
-                    while (bits) {
-                        const int j = 32 * w + __builtin_ctz(bits);   // 4 page + i
-                        bits &= bits - 1u;
-                        const int pg = j >> 2;
-                        uint32_t f = e;
+            for (int w = 0; w < 4; ++w) {
+                uint32_t bits = taken[w];
+                while (bits) {
+                    const int j = 32 * w + __builtin_ctz(bits);       // 4 page + i
+                    bits &= bits - 1u;
+                    const int pg = j >> 2;
+                    // other lanes' tokens below this one: their bits below 4 pg, and
+                    // for the lower quads also their bits of page pg
+                    const int b_lo = 4 * (pg & 7);
+                    const uint32_t m_hi = (1u << b_lo) - 1u;                           // bits < 4 pg
+                    const uint32_t m_lo = b_lo + 4 >= 32 ? 0xFFFFFFFFu : (1u << (b_lo + 4)) - 1u;
+                    uint32_t f = e + before_word[w];
 #pragma unroll
-                        for (int q2 = 0; q2 < 4; ++q2) {
-                            if (q2 == quad) continue;
-                            const int lim = 4 * pg + (q2 < quad ? 4 : 0);   // their bits below lim
-#pragma unroll
-                            for (int w2 = 0; w2 < 4; ++w2) {
-                                const int lo_bit = lim - 32 * w2;
-                                const uint32_t m = lo_bit >= 32 ? 0xFFFFFFFFu
-                                                 : lo_bit <= 0 ? 0u : ((1u << lo_bit) - 1u);
-                                f += (uint32_t)__popc(om[q2][w2] & m);
-                            }
-                        }
-                        const uint32_t key = score_key(__uint_as_float(ck[my_list + e]));
-                        kmax = max(kmax, key);
-                        cand_key[row * kCandCap + f] = key;
-                        cand_pos[row * kCandCap + f] = (uint16_t)(pg * kPage + 4 * quad + (j & 3));
-                        ++e;
-                    }
+                    for (int q2 = 0; q2 < 4; ++q2)
+                        if (q2 != quad) f += (uint32_t)__popc(om[q2][w] & (q2 < quad ? m_lo : m_hi));
+                    const uint32_t key = score_key(__uint_as_float(ck[my_list + e]));
+                    kmax = max(kmax, key);
+                    out_key[col * kCandCap + f] = key;
+                    tail_pos[f] = (uint16_t)(pg * kPage + 4 * quad + (j & 3));
+                    ++e;
                 }
             }
         }
@@ -473,7 +486,18 @@ __global__ __launch_bounds__(kScoreWaves * 64, 2) void score_kernel(
         uint32_t hm = 0;
 #pragma unroll
         for (int q2 = 0; q2 < 4; ++q2) hm = max(hm, (uint32_t)__shfl((int)kmax, col + 16 * q2, 64));
-        if (head_lane && quad == 0) cand_hi[row] = hm;
+        if (head_lane && quad == 0) *(u32x4 *)tail = u32x4{ovf ? kCandOverflow : total, lo, hm, 0u};
+        wave_lds_sync();
+        // 16 B per lane: lanes 0..47 the key lines, then lanes 0..31 the tail lines
+        for (int hh = 0; hh < heads_here; ++hh) {
+            const uint32_t tot = (uint32_t)__shfl((int)(ovf ? 0u : total), hh, 64);
+            u32x4 *rec = (u32x4 *)(cand_rec + (((int64_t)b * num_q_heads + h0 + hh) * slots + slot) * kRecWords);
+            const int key_chunks = (int)((tot + 31u) / 32u) * 8;                  // whole lines of keys
+            const int tail_chunks = (int)((4u + (tot + 1u) / 2u + 31u) / 32u) * 8; // header + positions
+            if (lane < key_chunks) rec[lane] = ((const u32x4 *)(out_key + hh * kCandCap))[lane];
+            if (lane < tail_chunks)
+                rec[kCandCap / 4 + lane] = ((const u32x4 *)(out_tail + hh * kRecTailWords))[lane];
+        }
     }
 }
 
@@ -497,14 +521,46 @@ __device__ __forceinline__ int load_keys8(const uint32_t *src, int start, int n,
 struct RowKeys {
     const uint32_t *key;
     __device__ int load8(int start, int n, uint32_t (&v)[8]) const { return load_keys8(key, start, n, v); }
-    __device__ int32_t token(int pos) const { return pos; }
+    __device__ void tokens8(int start, int cnt, int32_t (&t)[8]) const
+    {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) t[e] = start + e;
+    }
 };
 
-// Candidates gathered into LDS in token order, with their tokens.
+// Candidate keys gathered into LDS in token order.  The candidates of slot i are
+// positions [first[i], first[i + 1]); a token is found from its slot's record.
 struct LdsCandidates {
-    const uint32_t *key, *tok;
+    const uint32_t *key, *first;
+    const uint32_t *rec_row;                                  // the row's slot records
+    int nslots;
     __device__ int load8(int start, int n, uint32_t (&v)[8]) const { return load_keys8(key, start, n, v); }
-    __device__ int32_t token(int pos) const { return (int32_t)tok[pos]; }
+    // tokens of positions start .. start + cnt - 1 (cnt <= 8, all below first[nslots])
+    __device__ void tokens8(int start, int cnt, int32_t (&t)[8]) const
+    {
+        int lo = 0, hi = nslots;                              // first[lo] <= start < first[hi]
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (first[mid] <= (uint32_t)start) lo = mid; else hi = mid;
+        }
+        int i = lo;
+        uint32_t f0 = first[i], f1 = first[i + 1];
+        int slot_of[8], j_of[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const uint32_t v = (uint32_t)(start + e);
+            if (e < cnt) {
+                while (v >= f1) { ++i; f0 = f1; f1 = first[i + 1]; }
+            }
+            slot_of[e] = i;
+            j_of[e] = e < cnt ? (int)(v - f0) : 0;
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const uint16_t *pos = (const uint16_t *)(rec_row + (int64_t)slot_of[e] * kRecWords + kCandCap + 4);
+            t[e] = e < cnt ? slot_of[e] * kWaveTokens + pos[j_of[e]] : -1;
+        }
+    }
 };
 
 template <class Src>
@@ -576,6 +632,8 @@ __device__ __forceinline__ void compact_selected(const Src &src, int n, int kk, 
             gt += (e < cnt && v[e] > T) ? 1u : 0u;
             eq += (e < cnt && v[e] == T) ? 1u : 0u;
         }
+        int32_t tk[8];
+        if (gt + eq > 0u) src.tokens8(start, cnt, tk);        // loads in flight before the scan
         uint32_t tot;
         const uint32_t pre = block_exclusive_scan<kSelThreads>((eq << 16) | gt, scratch, tot);
         const uint32_t eq_left = r > run_eq ? r - run_eq : 0u;
@@ -587,7 +645,7 @@ __device__ __forceinline__ void compact_selected(const Src &src, int n, int kk, 
                 bool take = v[e] > T;
                 if (v[e] == T) take = (eq_rank++ < r);
                 if (take) {
-                    if (pos < (uint32_t)kk) out[pos] = src.token(start + e);
+                    if (pos < (uint32_t)kk) out[pos] = tk[e];
                     ++pos;
                 }
             }
@@ -602,11 +660,7 @@ struct SelectArgs {
     const uint16_t *kc;
     const int32_t *page_table, *seq_lens, *k_per_seq;
     const uint16_t *q;
-    const uint32_t *cand_key;                                 // [row][slot][kCandCap]
-    const uint16_t *cand_pos;                                 // token - 512 slot, same layout
-    const uint32_t *cand_cnt;                                 // [row][slot]
-    const uint32_t *cand_lo;                                  // [row][slot]: the slot's bound
-    const uint32_t *cand_hi;                                  // [row][slot]: its largest candidate key
+    const uint32_t *cand_rec;                                 // [row][slot] records of kRecWords
     int slots;                                                // slots per row
     int cap;                                                  // candidates the LDS holds (0: generic only)
     uint32_t *keys32;                                         // generic-path scratch, one row per (b, h)
@@ -647,7 +701,7 @@ __device__ __forceinline__ void select_rescore_generic(const SelectArgs &a, int6
 // grid (num_q_heads, batch); kSelThreads threads; dynamic LDS holds the candidates.
 __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a)
 {
-    extern __shared__ __attribute__((aligned(16))) uint32_t dyn_lds[];   // keys[cap] | tokens[cap]
+    extern __shared__ __attribute__((aligned(16))) uint32_t dyn_lds[];   // keys[cap] | first[slots + 1]
     __shared__ __attribute__((aligned(16))) uint32_t hist[kHistBins];
     __shared__ uint32_t scratch[kSelWaves + 2];
     __shared__ uint32_t res[8];
@@ -664,16 +718,14 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a)
         return;
     }
     bool generic = a.cap == 0;
-    uint32_t *ckey = dyn_lds, *ctok = dyn_lds + a.cap;
+    uint32_t *ckey = dyn_lds, *first = dyn_lds + a.cap;
     const int nslots = (n + kWaveTokens - 1) / kWaveTokens;
     uint32_t total = 0;
     if (threadIdx.x < 8) res[threadIdx.x] = threadIdx.x == 5 ? 0xFFFFFFFFu : 0u;
     if (!generic) {
-        // 1. slot counts -> each candidate's place; slot i writes the workspace offsets of
-        //    its entries (i * kCandCap + j) at their places in ctok, the gather map.  An
+        // 1. slot counts -> first[i], the place of slot i's first candidate.  An
         //    overflowed slot sends the row to the generic path.
-        const uint32_t *cnt_row = a.cand_cnt + bh * a.slots, *lo_row = a.cand_lo + bh * a.slots;
-        const uint32_t *hi_row = a.cand_hi + bh * a.slots;
+        const uint32_t *rec_row = a.cand_rec + bh * a.slots * kRecWords;
         int bad = 0;
         uint32_t lo_min = 0xFFFFFFFFu, lo_max = 0u, hi_max = 0u;
         for (int i = threadIdx.x; i < kHistBins; i += kSelThreads) hist[i] = 0u;
@@ -681,8 +733,9 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a)
             // loaded for every allocated slot (no wait for seq_lens), used below nslots
             const int i = base + (int)threadIdx.x;
             const bool in_ws = i < a.slots;
-            const uint32_t c_raw = in_ws ? cnt_row[i] : 0u, l = in_ws ? lo_row[i] : 0u;
-            const uint32_t hv = in_ws ? hi_row[i] : 0u;
+            const u32x4 hdr = in_ws ? *(const u32x4 *)(rec_row + (int64_t)i * kRecWords + kCandCap)
+                                    : u32x4{0u, 0u, 0u, 0u};
+            const uint32_t c_raw = hdr.x, l = hdr.y, hv = hdr.z;
             uint32_t c = i < nslots ? c_raw : 0u;
             if (i < nslots) {
                 lo_min = min(lo_min, l);
@@ -694,10 +747,10 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a)
             bad |= __syncthreads_or(ovf ? 1 : 0);
             uint32_t tot;
             const uint32_t p0 = total + block_exclusive_scan<kSelThreads>(c, scratch, tot);
-            for (uint32_t j = 0; j < c; ++j)
-                if (p0 + j < (uint32_t)a.cap) ctok[p0 + j] = (uint32_t)i * kCandCap + j;
+            if (in_ws) first[i] = p0;
             total += tot;
         }
+        if (threadIdx.x == 0) first[a.slots] = total;
         generic = bad != 0 || total < (uint32_t)kk || total > (uint32_t)a.cap;
 #pragma unroll
         for (int m = 32; m >= 1; m >>= 1) {
@@ -716,34 +769,34 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a)
         select_rescore_generic(a, bh, b, h, n, kk, hist, scratch, res, out);
         return;
     }
-    // 2. gather the candidates into LDS, in token order (4 loads per thread in flight),
-    //    counting the first radix digit of d = key - lo on the way: lo is the smallest
-    //    bound, and the largest candidate key gives the digits' span (bits)
+    // 2. gather the candidate keys into LDS in token order, one thread per slot (its
+    //    list in 16-byte pieces, all in flight), counting the first radix digit of
+    //    d = key - lo on the way: lo is the smallest bound, and the largest candidate
+    //    key gives the digits' span (bits)
     const uint32_t lo = res[5], lo_max = res[6];
     const int bits = 32 - __clz((int)(res[7] - lo));
     const int w0 = min(12, bits), sh0 = bits - w0;
     const uint32_t mask0 = (1u << w0) - 1u;
-    const uint32_t *key_row = a.cand_key + bh * a.slots * kCandCap;
-    const uint16_t *pos_row = a.cand_pos + bh * a.slots * kCandCap;
-    for (uint32_t v0 = 0; v0 < total; v0 += 4 * kSelThreads) {
-        uint32_t av[4], kv[4], tv[4];
+    const uint32_t *rec_row = a.cand_rec + bh * a.slots * kRecWords;
+    for (int i = threadIdx.x; i < nslots; i += kSelThreads) {
+        const uint32_t p0 = first[i], c = first[i + 1] - p0;
+        const uint32_t *keys = rec_row + (int64_t)i * kRecWords;
+        for (uint32_t j0 = 0; j0 < c; j0 += 32) {
+            u32x4 k4[8];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const uint32_t v = v0 + u * kSelThreads + threadIdx.x;
-            av[u] = v < total ? ctok[v] : 0u;
-        }
+            for (int u = 0; u < 8; ++u)
+                if (j0 + 4 * u < c) k4[u] = *(const u32x4 *)(keys + j0 + 4 * u);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const uint32_t v = v0 + u * kSelThreads + threadIdx.x;
-            if (v < total) { kv[u] = key_row[av[u]]; tv[u] = pos_row[av[u]]; }
-        }
+            for (int u = 0; u < 8; ++u) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const uint32_t v = v0 + u * kSelThreads + threadIdx.x;
-            if (v < total) {
-                ckey[v] = kv[u];
-                ctok[v] = (av[u] / kCandCap) * kWaveTokens + tv[u];
-                if (bits > 0) atomicAdd(&hist[((kv[u] - lo) >> sh0) & mask0], 1u);
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t j = j0 + 4 * u + e;
+                    if (j < c) {
+                        const uint32_t key = k4[u][e];
+                        ckey[p0 + j] = key;
+                        if (bits > 0) atomicAdd(&hist[((key - lo) >> sh0) & mask0], 1u);
+                    }
+                }
             }
         }
     }
@@ -754,7 +807,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a)
     //    already reaches every bound, the bin floor is T with all ties; otherwise the
     //    bin's few entries are ranked exactly by one wave.  The selection is valid if T
     //    reaches every workgroup bound.
-    const LdsCandidates cands{ckey, ctok};
+    const LdsCandidates cands{ckey, first, rec_row, nslots};
     uint32_t T = lo, r = (uint32_t)kk;
     if (bits > 0) {
         threshold_bin_wave(hist, max(64, 1 << w0), (uint32_t)kk, res);
@@ -812,12 +865,10 @@ static int index_topk_slots(int n_max) { return (n_max + kWaveTokens - 1) / kWav
 
 size_t index_topk_workspace_bytes(int batch, int num_q_heads, int n_max)
 {
-    // per (b, h): a 32-bit key row for the generic path, then per 512-token slot the
-    // candidate list (32-bit keys, 16-bit positions), its count, its bound and its
-    // largest key
+    // per (b, h): a 32-bit key row for the generic path, then per 512-token slot a
+    // candidate record (count, bound, largest key, 32-bit keys, 16-bit positions)
     const size_t rows = (size_t)batch * num_q_heads, slots = (size_t)index_topk_slots(n_max);
-    return rows * (index_topk_key_stride(n_max) * sizeof(uint32_t) +
-                   slots * (kCandCap * (sizeof(uint32_t) + sizeof(uint16_t)) + 3 * sizeof(uint32_t)));
+    return rows * (index_topk_key_stride(n_max) * sizeof(uint32_t) + slots * kRecWords * sizeof(uint32_t));
 }
 
 hipError_t launch_index_topk(const IndexArgs &a, hipStream_t stream)
@@ -828,17 +879,12 @@ hipError_t launch_index_topk(const IndexArgs &a, hipStream_t stream)
     const int slots = index_topk_slots(a.n_max);
     const size_t rows = (size_t)a.batch * a.num_q_heads;
     uint32_t *keys32 = (uint32_t *)a.ws;
-    uint32_t *cand_key = keys32 + rows * stride;
-    uint32_t *cand_cnt = cand_key + rows * slots * kCandCap;
-    uint32_t *cand_lo = cand_cnt + rows * slots;
-    uint32_t *cand_hi = cand_lo + rows * slots;
-    uint16_t *cand_pos = (uint16_t *)(cand_hi + rows * slots);
+    uint32_t *cand_rec = keys32 + rows * stride;              // 512 B multiple: records start on lines
 
     dim3 sgrid((a.n_max + kScoreTokensPerBlock - 1) / kScoreTokensPerBlock, a.num_kv_heads * head_blocks, a.batch);
     hipLaunchKernelGGL(score_kernel, sgrid, dim3(kScoreWaves * 64), 0, stream, (const uint16_t *)a.k_cache,
                        a.page_table, a.seq_lens, (const uint16_t *)a.q, a.k_per_seq, a.num_q_heads,
-                       a.num_kv_heads, group, head_blocks, a.max_pages, a.k_max, cand_key, cand_pos, cand_cnt,
-                       cand_lo, cand_hi, slots);
+                       a.num_kv_heads, group, head_blocks, a.max_pages, a.k_max, cand_rec, slots);
 
     // LDS for the candidates.  A workgroup's bound is reached by about (n_w / 1024) r
     // of its n_w tokens, r = mu + 6 sqrt(mu) + 8 and mu = 1024 k / n, so a row has
@@ -846,8 +892,11 @@ hipError_t launch_index_topk(const IndexArgs &a, hipStream_t stream)
     // (15% margin).  Rows beyond the capacity take the re-scoring path.
     const double kd = a.k_max, nd = a.n_max;
     const double expect = kd + 6.0 * std::sqrt(kd * nd / 1024.0) + 8.0 * nd / 1024.0;
-    const int cap = (int)std::min<double>(kSelCapMax, std::ceil(1.15 * expect) + 256.0);
-    const size_t dyn = (size_t)cap * 2 * sizeof(uint32_t);
+    // The slot starts take (slots + 1) words beside the keys; a row so long that they
+    // crowd the keys out takes the re-scoring path (cap 0).
+    const int cap = std::max(0, std::min((int)std::min<double>(kSelCapMax, std::ceil(1.15 * expect) + 256.0),
+                                         (int)(kSelDynMax / sizeof(uint32_t)) - (slots + 1)));
+    const size_t dyn = cap == 0 ? 0 : (size_t)(cap + slots + 1) * sizeof(uint32_t);
     if (dyn > 64 * 1024) {
         // raise the kernel's dynamic-LDS limit to the budget once (a function attribute,
         // not a stream operation)
@@ -860,7 +909,7 @@ hipError_t launch_index_topk(const IndexArgs &a, hipStream_t stream)
         }
     }
     SelectArgs s{(const uint16_t *)a.k_cache, a.page_table, a.seq_lens, a.k_per_seq, (const uint16_t *)a.q,
-                 cand_key, cand_pos, cand_cnt, cand_lo, cand_hi, slots, cap, keys32, stride, a.num_q_heads, a.num_kv_heads,
+                 cand_rec, slots, cap, keys32, stride, a.num_q_heads, a.num_kv_heads,
                  group, a.max_pages, a.k_max, a.idx_out};
     hipLaunchKernelGGL(select_kernel, dim3(a.num_q_heads, a.batch), dim3(kSelThreads), dyn, stream, s);
     return hipGetLastError();

@@ -52,9 +52,10 @@ def test_strerror_covers_every_code(lib):
 def test_workspace_sizes(lib):
     k = kv()
     n1 = lib.sparse_decode_index_topk_workspace(ctypes.byref(k), 8, 5)
-    # per row: a 32-bit key row (padded to 128 tokens), then per 512-token slot 192 candidates
-    # (32-bit key + 16-bit position), a count, the slot's lower bound and its largest key
-    assert n1 == 2 * 8 * (256 * 4 + 1 * (192 * 6 + 12))
+    # per row: a 32-bit key row (padded to 128 tokens), then per 512-token slot a 1280-byte
+    # record: 192 32-bit keys, a count, the slot's lower bound, its largest key, a pad word
+    # and 192 16-bit positions, padded to whole 128-byte lines
+    assert n1 == 2 * 8 * (256 * 4 + 1 * 1280)
     assert lib.sparse_decode_attend_workspace(ctypes.byref(k), 8, 1024) == 0         # one chunk: no partials
     assert lib.sparse_decode_attend_workspace(ctypes.byref(k), 8, 1025) == 2 * 8 * 5 * 130 * 4   # 256-entry chunks
     assert lib.dense_decode_workspace(ctypes.byref(k), 8) == 2 * 8 * 1 * 130 * 4      # one 1024-token chunk
