@@ -41,10 +41,12 @@
 
 #include <atomic>
 #include <cmath>
+#include <type_traits>
 
 namespace sdi {
 
 constexpr int kHeadBlock = 8;                                 // query heads scored per workgroup
+constexpr int kCUs = 256;                                     // MI355X compute units
 
 // ---- score pass --------------------------------------------------------------------------
 constexpr int kScoreWaves = 4;                                // two workgroups per CU (LDS < 80 KB each)
@@ -193,13 +195,14 @@ __device__ __forceinline__ void threshold_bin_wave(const uint32_t *hist, int nbi
 // ---- 1. score pass -----------------------------------------------------------------------
 
 // grid (ceil(n_max / 2048), kv_heads * head_blocks, batch); 256 threads.
+template <int kSlots>
 __global__ __launch_bounds__(kScoreWaves * 64, 2) void score_kernel(
     const uint16_t *__restrict__ kc, const int32_t *__restrict__ page_table,
     const int32_t *__restrict__ seq_lens, const uint16_t *__restrict__ q, const int32_t *__restrict__ k_per_seq,
     int num_q_heads, int num_kv_heads, int group, int head_blocks, int max_pages, int k_max,
     uint32_t *__restrict__ cand_rec, int slots)
 {
-    __shared__ int32_t pt_lds[kScoreWaves * kScorePagesPerWave];
+    __shared__ int32_t pt_lds[kSlots * kScoreWaves * kScorePagesPerWave];
     __shared__ __attribute__((aligned(16))) unsigned char stage_all[kScoreWaves * kScoreUnroll * kStagePage];
     __shared__ uint32_t ck_all[kScoreWaves * kHeadBlock * 4 * kSubStride];
     __shared__ __attribute__((aligned(16))) uint16_t samp[kHeadBlock][kBlockSample];   // top 16 key bits
@@ -208,7 +211,8 @@ __global__ __launch_bounds__(kScoreWaves * 64, 2) void score_kernel(
     const int b = blockIdx.z;
     const int g = blockIdx.y / head_blocks, hb = blockIdx.y - g * head_blocks;
     const int n = seq_lens[b];
-    const int tok0 = blockIdx.x * kScoreTokensPerBlock;
+    static_assert(kSlots >= 1 && kSlots <= 4, "1 to 4 slots per wave");
+    const int tok0 = blockIdx.x * kSlots * kScoreTokensPerBlock;
     if (tok0 >= n) return;                                    // whole block exits together
     const int kk = min(min(k_per_seq[b], n), k_max);
     const int heads_here = min(kHeadBlock, group - hb * kHeadBlock);
@@ -223,13 +227,17 @@ __global__ __launch_bounds__(kScoreWaves * 64, 2) void score_kernel(
 
     const int pages_seq = (n + kPage - 1) / kPage;
     const int p_base = tok0 / kPage;                          // first page of this workgroup
-    const int p_begin = p_base + wave * kScorePagesPerWave;
-    const int p_end = min(p_begin + kScorePagesPerWave, pages_seq);
+    // slot s of this wave is the workgroup's slot 4 s + wave: pages p_begin .. p_end - 1
+    auto slot_begin = [&](int sl) { return p_base + (sl * kScoreWaves + wave) * kScorePagesPerWave; };
+    auto slot_end = [&](int sl) { return min(slot_begin(sl) + kScorePagesPerWave, pages_seq); };
+    int p_begin = slot_begin(0), p_end = slot_end(0);
     const bool has_pages = p_begin < p_end;                   // wave-uniform
     {
         const int32_t *pt = page_table + (int64_t)b * max_pages;
         const int i = threadIdx.x;
-        if (i < kScoreWaves * kScorePagesPerWave && p_base + i < pages_seq) pt_lds[i] = pt[p_base + i];
+#pragma unroll
+        for (int j = i; j < kSlots * kScoreWaves * kScorePagesPerWave; j += kScoreWaves * 64)
+            if (p_base + j < pages_seq) pt_lds[j] = pt[p_base + j];
         // the head block's q rows (16 B per thread), staged with the page slice
         if (i < heads_here * (kHeadDim / 8))
             *(u32x4 *)(q_lds + i * 8) = *(const u32x4 *)(q + ((int64_t)b * num_q_heads + h0) * kHeadDim + i * 8);
@@ -253,10 +261,11 @@ __global__ __launch_bounds__(kScoreWaves * 64, 2) void score_kernel(
     uint32_t lo = 0xFFFFFFFFu;                                // head col's bound (set after the sample)
     float lo_f = __builtin_nanf("");                          // the smallest score whose key reaches lo
 
-    auto load_group = [&](u32x4 (&kr)[kScoreUnroll][4], int p) {
+    // pages p, p + 1, clamped to pend - 1 (a group past the row re-reads a page of it)
+    auto load_group = [&](u32x4 (&kr)[kScoreUnroll][4], int p, int pend) {
         int64_t phys[kScoreUnroll];
 #pragma unroll
-        for (int u = 0; u < kScoreUnroll; ++u) phys[u] = pt_lds[min(p + u, p_end - 1) - p_base];
+        for (int u = 0; u < kScoreUnroll; ++u) phys[u] = pt_lds[min(p + u, pend - 1) - p_base];
 #pragma unroll
         for (int u = 0; u < kScoreUnroll; ++u) {
             const u32x4 *src = (const u32x4 *)(k_head + phys[u] * page_elems) + lane;
@@ -306,10 +315,10 @@ __global__ __launch_bounds__(kScoreWaves * 64, 2) void score_kernel(
             cnt += take ? 1u : 0u;
         }
     };
-    auto score_group = [&](u32x4 (&kr)[kScoreUnroll][4], int p, int p_next, bool reload) {
+    auto score_group = [&](u32x4 (&kr)[kScoreUnroll][4], int p, int p_next, int pend_next, bool reload) {
         stage_group(kr);
         sched_fence();
-        if (reload) load_group(kr, p_next);
+        if (reload) load_group(kr, p_next, pend_next);
         sched_fence();
         // the operands of every staged page first: LDS operations complete in order, so
         // an operand read issued after an append's writes would wait for them
@@ -333,7 +342,7 @@ __global__ __launch_bounds__(kScoreWaves * 64, 2) void score_kernel(
     auto sample_group = [&](u32x4 (&kr)[kScoreUnroll][4], int su0) {
         stage_group(kr);                                      // (a wave without pages stages
         sched_fence();                                        //  and loads its row's last page)
-        load_group(kr, p_begin + su0 + 2 * kScoreUnroll);
+        load_group(kr, p_begin + su0 + 2 * kScoreUnroll, p_end);
         sched_fence();
 #pragma unroll
         for (int u = 0; u < kScoreUnroll; ++u) {
@@ -354,9 +363,9 @@ __global__ __launch_bounds__(kScoreWaves * 64, 2) void score_kernel(
 
     // 1. the sample pages, with the next group's loads in flight
     u32x4 ka[kScoreUnroll][4], kb[kScoreUnroll][4];
-    load_group(ka, p_begin);                                  // unconditional: no control flow
+    load_group(ka, p_begin, p_end);                           // unconditional: no control flow
     sched_fence();                                            // around loads in flight
-    load_group(kb, p_begin + kScoreUnroll);
+    load_group(kb, p_begin + kScoreUnroll, p_end);
     sched_fence();
 #pragma unroll
     for (int gi = 0; gi < kSampleGroups; gi += 2) {
@@ -409,17 +418,7 @@ __global__ __launch_bounds__(kScoreWaves * 64, 2) void score_kernel(
 #pragma unroll
     for (int su = 0; su < kSamplePagesPerWave; ++su)
         if (p_begin + su < p_end) append_page(skey[su], su);
-    if (has_pages) {                                          // wave-uniform
-        // fully unrolled: straight-line code lets the compiler wait for exactly the
-        // group it stages, with the next two groups still in flight
-        constexpr int kMainIters = (kScorePagesPerWave - kSamplePagesPerWave) / (2 * kScoreUnroll);
-#pragma unroll
-        for (int it = 0; it < kMainIters; ++it) {
-            const int o = kSamplePagesPerWave + it * 2 * kScoreUnroll;     // page offset in the wave
-            const int p = p_begin + o;
-            score_group(ka, p, p + 2 * kScoreUnroll, o + 2 * kScoreUnroll < kScorePagesPerWave);
-            score_group(kb, p + kScoreUnroll, p + 3 * kScoreUnroll, o + 3 * kScoreUnroll < kScorePagesPerWave);
-        }
+    auto flush_slot = [&]() {
         // this wave's slot: per head one record (count, bound, largest key, then the
         // candidates in token order).  Head lane (col, quad) places its own entries:
         // the e-th set bit of its mask is the token of its e-th entry, which goes to
@@ -498,6 +497,44 @@ __global__ __launch_bounds__(kScoreWaves * 64, 2) void score_kernel(
             if (lane < tail_chunks)
                 rec[kCandCap / 4 + lane] = ((const u32x4 *)(out_tail + hh * kRecTailWords))[lane];
         }
+    };
+    // the main phase of slot S: its pages after the sample (slot 0) or all of them,
+    // fully unrolled: straight-line code lets the compiler wait for exactly the group it
+    // stages, with the next two groups in flight.  The last groups of a slot put the
+    // next slot's first pages in flight, so the flush overlaps their loads.
+    auto run_slot = [&](auto S) -> bool {
+        constexpr int sl = decltype(S)::value;
+        if constexpr (sl > 0) {
+            p_begin = slot_begin(sl);
+            p_end = slot_end(sl);
+            if (p_begin >= p_end) return false;               // wave-uniform; later slots are empty too
+            cnt = 0u;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) taken[w] = 0u;
+        }
+        constexpr bool more = sl + 1 < kSlots;
+        const int nb = more ? slot_begin(sl + 1) : 0, ne = more ? slot_end(sl + 1) : 0;
+        constexpr int o0 = sl == 0 ? kSamplePagesPerWave : 0;
+        constexpr int kIters = (kScorePagesPerWave - o0) / (2 * kScoreUnroll);
+#pragma unroll
+        for (int it = 0; it < kIters; ++it) {
+            const int o = o0 + it * 2 * kScoreUnroll;         // page offset in the slot
+            const int p = p_begin + o;
+            const int oa = o + 2 * kScoreUnroll, ob = o + 3 * kScoreUnroll;
+            score_group(ka, p, oa < kScorePagesPerWave ? p_begin + oa : nb + oa - kScorePagesPerWave,
+                        oa < kScorePagesPerWave ? p_end : ne, oa < kScorePagesPerWave || more);
+            score_group(kb, p + kScoreUnroll, ob < kScorePagesPerWave ? p_begin + ob : nb + ob - kScorePagesPerWave,
+                        ob < kScorePagesPerWave ? p_end : ne, ob < kScorePagesPerWave || more);
+        }
+        flush_slot();
+        return true;
+    };
+    if (has_pages) {                                          // wave-uniform
+        bool go = run_slot(std::integral_constant<int, 0>{});
+        if constexpr (kSlots > 1) go = go && run_slot(std::integral_constant<int, 1>{});
+        if constexpr (kSlots > 2) go = go && run_slot(std::integral_constant<int, 2>{});
+        if constexpr (kSlots > 3) go = go && run_slot(std::integral_constant<int, 3>{});
+        (void)go;
     }
 }
 
@@ -529,21 +566,16 @@ struct RowKeys {
 };
 
 // Candidate keys gathered into LDS in token order.  The candidates of slot i are
-// positions [first[i], first[i + 1]); a token is found from its slot's record.
+// positions [first[i], first[i + 1]); blk[v / 64] is the slot of position 64 (v / 64),
+// where the walk to position v's slot starts.  A token is found from its slot's record.
 struct LdsCandidates {
-    const uint32_t *key, *first;
+    const uint32_t *key, *first, *blk;
     const uint32_t *rec_row;                                  // the row's slot records
-    int nslots;
     __device__ int load8(int start, int n, uint32_t (&v)[8]) const { return load_keys8(key, start, n, v); }
-    // tokens of positions start .. start + cnt - 1 (cnt <= 8, all below first[nslots])
+    // tokens of positions start .. start + cnt - 1 (cnt <= 8, all below the total)
     __device__ void tokens8(int start, int cnt, int32_t (&t)[8]) const
     {
-        int lo = 0, hi = nslots;                              // first[lo] <= start < first[hi]
-        while (hi - lo > 1) {
-            const int mid = (lo + hi) >> 1;
-            if (first[mid] <= (uint32_t)start) lo = mid; else hi = mid;
-        }
-        int i = lo;
+        int i = (int)blk[start >> 6];
         uint32_t f0 = first[i], f1 = first[i + 1];
         int slot_of[8], j_of[8];
 #pragma unroll
@@ -701,7 +733,7 @@ __device__ __forceinline__ void select_rescore_generic(const SelectArgs &a, int6
 // grid (num_q_heads, batch); kSelThreads threads; dynamic LDS holds the candidates.
 __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a)
 {
-    extern __shared__ __attribute__((aligned(16))) uint32_t dyn_lds[];   // keys[cap] | first[slots + 1]
+    extern __shared__ __attribute__((aligned(16))) uint32_t dyn_lds[];   // keys[cap] | first[slots + 1] | blk
     __shared__ __attribute__((aligned(16))) uint32_t hist[kHistBins];
     __shared__ uint32_t scratch[kSelWaves + 2];
     __shared__ uint32_t res[8];
@@ -709,6 +741,10 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a)
 
     const int h = blockIdx.x, b = blockIdx.y;
     const int64_t bh = (int64_t)b * a.num_q_heads + h;
+    const uint32_t *rec_row = a.cand_rec + bh * a.slots * kRecWords;
+    // the first block of slot headers goes out before the row's length arrives
+    u32x4 hdr0 = u32x4{0u, 0u, 0u, 0u};
+    if (a.cap != 0 && (int)threadIdx.x < a.slots) hdr0 = *(const u32x4 *)(rec_row + threadIdx.x * kRecWords + kCandCap);
     const int n = a.seq_lens[b];
     int kk = min(min(a.k_per_seq[b], n), a.k_max);
     if (kk < 0) kk = 0;
@@ -718,14 +754,13 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a)
         return;
     }
     bool generic = a.cap == 0;
-    uint32_t *ckey = dyn_lds, *first = dyn_lds + a.cap;
+    uint32_t *ckey = dyn_lds, *first = dyn_lds + a.cap, *blk = first + a.slots + 1;
     const int nslots = (n + kWaveTokens - 1) / kWaveTokens;
     uint32_t total = 0;
     if (threadIdx.x < 8) res[threadIdx.x] = threadIdx.x == 5 ? 0xFFFFFFFFu : 0u;
     if (!generic) {
         // 1. slot counts -> first[i], the place of slot i's first candidate.  An
         //    overflowed slot sends the row to the generic path.
-        const uint32_t *rec_row = a.cand_rec + bh * a.slots * kRecWords;
         int bad = 0;
         uint32_t lo_min = 0xFFFFFFFFu, lo_max = 0u, hi_max = 0u;
         for (int i = threadIdx.x; i < kHistBins; i += kSelThreads) hist[i] = 0u;
@@ -733,8 +768,9 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a)
             // loaded for every allocated slot (no wait for seq_lens), used below nslots
             const int i = base + (int)threadIdx.x;
             const bool in_ws = i < a.slots;
-            const u32x4 hdr = in_ws ? *(const u32x4 *)(rec_row + (int64_t)i * kRecWords + kCandCap)
-                                    : u32x4{0u, 0u, 0u, 0u};
+            const u32x4 hdr = base == 0 ? hdr0
+                              : in_ws ? *(const u32x4 *)(rec_row + (int64_t)i * kRecWords + kCandCap)
+                                      : u32x4{0u, 0u, 0u, 0u};
             const uint32_t c_raw = hdr.x, l = hdr.y, hv = hdr.z;
             uint32_t c = i < nslots ? c_raw : 0u;
             if (i < nslots) {
@@ -748,6 +784,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a)
             uint32_t tot;
             const uint32_t p0 = total + block_exclusive_scan<kSelThreads>(c, scratch, tot);
             if (in_ws) first[i] = p0;
+            for (uint32_t v = (p0 + 63u) & ~63u; v < p0 + c && v < (uint32_t)a.cap; v += 64u) blk[v >> 6] = (uint32_t)i;
             total += tot;
         }
         if (threadIdx.x == 0) first[a.slots] = total;
@@ -777,7 +814,6 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a)
     const int bits = 32 - __clz((int)(res[7] - lo));
     const int w0 = min(12, bits), sh0 = bits - w0;
     const uint32_t mask0 = (1u << w0) - 1u;
-    const uint32_t *rec_row = a.cand_rec + bh * a.slots * kRecWords;
     for (int i = threadIdx.x; i < nslots; i += kSelThreads) {
         const uint32_t p0 = first[i], c = first[i + 1] - p0;
         const uint32_t *keys = rec_row + (int64_t)i * kRecWords;
@@ -807,7 +843,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a)
     //    already reaches every bound, the bin floor is T with all ties; otherwise the
     //    bin's few entries are ranked exactly by one wave.  The selection is valid if T
     //    reaches every workgroup bound.
-    const LdsCandidates cands{ckey, first, rec_row, nslots};
+    const LdsCandidates cands{ckey, first, blk, rec_row};
     uint32_t T = lo, r = (uint32_t)kk;
     if (bits > 0) {
         threshold_bin_wave(hist, max(64, 1 << w0), (uint32_t)kk, res);
@@ -881,10 +917,23 @@ hipError_t launch_index_topk(const IndexArgs &a, hipStream_t stream)
     uint32_t *keys32 = (uint32_t *)a.ws;
     uint32_t *cand_rec = keys32 + rows * stride;              // 512 B multiple: records start on lines
 
-    dim3 sgrid((a.n_max + kScoreTokensPerBlock - 1) / kScoreTokensPerBlock, a.num_kv_heads * head_blocks, a.batch);
-    hipLaunchKernelGGL(score_kernel, sgrid, dim3(kScoreWaves * 64), 0, stream, (const uint16_t *)a.k_cache,
-                       a.page_table, a.seq_lens, (const uint16_t *)a.q, a.k_per_seq, a.num_q_heads,
-                       a.num_kv_heads, group, head_blocks, a.max_pages, a.k_max, cand_rec, slots);
+    // Two slots per wave when that gives every CU two workgroups for at most two rounds:
+    // a workgroup's first flush then overlaps its second half's loads, and half as many
+    // workgroups wait for their last stores.  Longer grids (many rounds of ragged rows)
+    // measured faster with one slot.
+    const int64_t blocks2 = (int64_t)((a.n_max + 2 * kScoreTokensPerBlock - 1) / (2 * kScoreTokensPerBlock)) *
+                            a.num_kv_heads * head_blocks * a.batch;
+    const bool two = blocks2 >= 2 * kCUs && blocks2 <= 4 * kCUs;
+    const int per_block = (two ? 2 : 1) * kScoreTokensPerBlock;
+    dim3 sgrid((a.n_max + per_block - 1) / per_block, a.num_kv_heads * head_blocks, a.batch);
+    if (two)
+        hipLaunchKernelGGL(score_kernel<2>, sgrid, dim3(kScoreWaves * 64), 0, stream, (const uint16_t *)a.k_cache,
+                           a.page_table, a.seq_lens, (const uint16_t *)a.q, a.k_per_seq, a.num_q_heads,
+                           a.num_kv_heads, group, head_blocks, a.max_pages, a.k_max, cand_rec, slots);
+    else
+        hipLaunchKernelGGL(score_kernel<1>, sgrid, dim3(kScoreWaves * 64), 0, stream, (const uint16_t *)a.k_cache,
+                           a.page_table, a.seq_lens, (const uint16_t *)a.q, a.k_per_seq, a.num_q_heads,
+                           a.num_kv_heads, group, head_blocks, a.max_pages, a.k_max, cand_rec, slots);
 
     // LDS for the candidates.  A workgroup's bound is reached by about (n_w / 1024) r
     // of its n_w tokens, r = mu + 6 sqrt(mu) + 8 and mu = 1024 k / n, so a row has
@@ -892,11 +941,11 @@ hipError_t launch_index_topk(const IndexArgs &a, hipStream_t stream)
     // (15% margin).  Rows beyond the capacity take the re-scoring path.
     const double kd = a.k_max, nd = a.n_max;
     const double expect = kd + 6.0 * std::sqrt(kd * nd / 1024.0) + 8.0 * nd / 1024.0;
-    // The slot starts take (slots + 1) words beside the keys; a row so long that they
-    // crowd the keys out takes the re-scoring path (cap 0).
-    const int cap = std::max(0, std::min((int)std::min<double>(kSelCapMax, std::ceil(1.15 * expect) + 256.0),
-                                         (int)(kSelDynMax / sizeof(uint32_t)) - (slots + 1)));
-    const size_t dyn = cap == 0 ? 0 : (size_t)(cap + slots + 1) * sizeof(uint32_t);
+    // Beside the keys, the slot starts take (slots + 1) words and the walk starts one
+    // word per 64 keys; rows so long that these crowd the keys out re-score (cap 0).
+    const int cap_lds = ((int)(kSelDynMax / sizeof(uint32_t)) - (slots + 2)) * 64 / 65;
+    const int cap = std::max(0, std::min((int)std::min<double>(kSelCapMax, std::ceil(1.15 * expect) + 256.0), cap_lds));
+    const size_t dyn = cap == 0 ? 0 : (size_t)(cap + slots + 1 + (cap + 63) / 64) * sizeof(uint32_t);
     if (dyn > 64 * 1024) {
         // raise the kernel's dynamic-LDS limit to the budget once (a function attribute,
         // not a stream operation)

@@ -66,6 +66,21 @@ def test_config_small(cfg, kw):
     run_and_check(dev, oracle.Cache.of(wl), wl.q, wl.k_per_seq(), wl.k_max(), tag=f"C{cfg}-small")
 
 
+@pytest.mark.parametrize("cfg,kw", [
+    (2, dict(n=8192, batch=32)),
+    (5, dict(n=4096, batch=64, steps=1)),
+], ids=["C2-B32", "C5-B64-ragged"])
+def test_two_slot_workgroups(cfg, kw):
+    """Grids of one or two rounds score two 512-token slots per wave (the first slot's
+    flush overlapping the second's loads); these shapes take that path, the ragged one
+    with waves whose second slot is partial or empty."""
+    wl = synth.config(cfg, **kw)
+    blocks2 = -(-wl.n_max // 4096) * wl.num_kv_heads * -(-wl.group // 8) * wl.batch
+    assert 2 * 256 <= blocks2 <= 4 * 256
+    dev = DeviceCase.of_workload(wl)
+    run_and_check(dev, oracle.Cache.of(wl), wl.q, wl.k_per_seq(), wl.k_max(), tag=f"C{cfg}-two-slot")
+
+
 def _append_on_device(dev, rows):
     tok, pages, slots, kr, vr = rows
     from device import bf16_tensor
