@@ -51,7 +51,9 @@ constexpr int kCUs = 256;                                     // MI355X compute 
 // ---- score pass --------------------------------------------------------------------------
 constexpr int kScoreWaves = 4;                                // two workgroups per CU (LDS < 80 KB each)
 constexpr int kScorePagesPerWave = 32;
-constexpr int kScoreUnroll = 2;                               // pages per register buffer
+constexpr int kScoreUnroll = 2;                               // pages per register buffer (a group)
+constexpr int kScoreBufs = 2;                                 // groups in flight per wave (3 measured no faster)
+constexpr int kSlotGroups = kScorePagesPerWave / kScoreUnroll;
 constexpr int kWaveTokens = kScorePagesPerWave * kPage;       // 512 tokens: one candidate slot
 constexpr int kScoreTokensPerBlock = kScoreWaves * kWaveTokens;
 constexpr int kStageRow = kRowBytes + 16;                     // padded LDS row: conflict-free both ways
@@ -121,6 +123,16 @@ __device__ __forceinline__ f32x4 rescore16(const uint16_t *__restrict__ kc, int 
 // score pass relies on program order (stage a group, put the next group in flight,
 // then score) so that each wait covers only the group being staged.
 __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
+
+// f(integral_constant<int, i>) for i = B .. E - 1, in order, at compile time.
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F &&f)
+{
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
+}
 
 __device__ __forceinline__ void wave_lds_sync()
 {
@@ -342,7 +354,7 @@ __global__ __launch_bounds__(kScoreWaves * 64, 2) void score_kernel(
     auto sample_group = [&](u32x4 (&kr)[kScoreUnroll][4], int su0) {
         stage_group(kr);                                      // (a wave without pages stages
         sched_fence();                                        //  and loads its row's last page)
-        load_group(kr, p_begin + su0 + 2 * kScoreUnroll, p_end);
+        load_group(kr, p_begin + su0 + kScoreBufs * kScoreUnroll, p_end);
         sched_fence();
 #pragma unroll
         for (int u = 0; u < kScoreUnroll; ++u) {
@@ -361,17 +373,20 @@ __global__ __launch_bounds__(kScoreWaves * 64, 2) void score_kernel(
         sched_fence();
     };
 
-    // 1. the sample pages, with the next group's loads in flight
-    u32x4 ka[kScoreUnroll][4], kb[kScoreUnroll][4];
-    load_group(ka, p_begin, p_end);                           // unconditional: no control flow
-    sched_fence();                                            // around loads in flight
-    load_group(kb, p_begin + kScoreUnroll, p_end);
-    sched_fence();
-#pragma unroll
-    for (int gi = 0; gi < kSampleGroups; gi += 2) {
-        sample_group(ka, gi * kScoreUnroll);
-        sample_group(kb, (gi + 1) * kScoreUnroll);
-    }
+    // 1. the sample pages, with the next groups' loads in flight.  Group G of the wave
+    //    (counted over its slots) lives in register buffer G mod kScoreBufs.
+    u32x4 kb0[kScoreUnroll][4], kb1[kScoreUnroll][4], kb2[kScoreUnroll][4];
+    auto buf = [&](auto G) -> u32x4 (&)[kScoreUnroll][4] {
+        constexpr int i = decltype(G)::value % kScoreBufs;
+        if constexpr (i == 0) return kb0;
+        else if constexpr (i == 1) return kb1;
+        else return kb2;
+    };
+    static_for<0, kScoreBufs>([&](auto G) {                   // unconditional: no control flow
+        load_group(buf(G), p_begin + decltype(G)::value * kScoreUnroll, p_end);   // around loads in flight
+        sched_fence();
+    });
+    static_for<0, kSampleGroups>([&](auto G) { sample_group(buf(G), decltype(G)::value * kScoreUnroll); });
     lds_barrier();
     // 2. per head hh (one wave each): its bound, the r-th largest sample code found by bisection,
     //    r = mu + 6 sqrt(mu) + 8 for mu the expected number of samples at or above
@@ -500,7 +515,7 @@ __global__ __launch_bounds__(kScoreWaves * 64, 2) void score_kernel(
     };
     // the main phase of slot S: its pages after the sample (slot 0) or all of them,
     // fully unrolled: straight-line code lets the compiler wait for exactly the group it
-    // stages, with the next two groups in flight.  The last groups of a slot put the
+    // stages, with the next groups in flight.  The last groups of a slot put the
     // next slot's first pages in flight, so the flush overlaps their loads.
     auto run_slot = [&](auto S) -> bool {
         constexpr int sl = decltype(S)::value;
@@ -514,18 +529,14 @@ __global__ __launch_bounds__(kScoreWaves * 64, 2) void score_kernel(
         }
         constexpr bool more = sl + 1 < kSlots;
         const int nb = more ? slot_begin(sl + 1) : 0, ne = more ? slot_end(sl + 1) : 0;
-        constexpr int o0 = sl == 0 ? kSamplePagesPerWave : 0;
-        constexpr int kIters = (kScorePagesPerWave - o0) / (2 * kScoreUnroll);
-#pragma unroll
-        for (int it = 0; it < kIters; ++it) {
-            const int o = o0 + it * 2 * kScoreUnroll;         // page offset in the slot
-            const int p = p_begin + o;
-            const int oa = o + 2 * kScoreUnroll, ob = o + 3 * kScoreUnroll;
-            score_group(ka, p, oa < kScorePagesPerWave ? p_begin + oa : nb + oa - kScorePagesPerWave,
-                        oa < kScorePagesPerWave ? p_end : ne, oa < kScorePagesPerWave || more);
-            score_group(kb, p + kScoreUnroll, ob < kScorePagesPerWave ? p_begin + ob : nb + ob - kScorePagesPerWave,
-                        ob < kScorePagesPerWave ? p_end : ne, ob < kScorePagesPerWave || more);
-        }
+        static_for<sl == 0 ? kSampleGroups : 0, kSlotGroups>([&](auto GI) {
+            constexpr int g = decltype(GI)::value;            // group in the slot
+            constexpr int gn = g + kScoreBufs;                // the group its buffer loads next
+            constexpr bool same = gn < kSlotGroups;
+            score_group(buf(std::integral_constant<int, sl * kSlotGroups + g>{}), p_begin + g * kScoreUnroll,
+                        same ? p_begin + gn * kScoreUnroll : nb + (gn - kSlotGroups) * kScoreUnroll,
+                        same ? p_end : ne, same || more);
+        });
         flush_slot();
         return true;
     };
