@@ -67,6 +67,10 @@ constexpr uint32_t kCandOverflow = 0xFFFFFFFFu;               // slot count of a
 // start) in token order.
 constexpr int kRecTailWords = 128;                            // 512 B: 4 header words + 192 positions
 constexpr int kRecWords = kCandCap + kRecTailWords;
+// Buffer resource word 3 for untyped 32-bit accesses on gfx9, and an offset past any
+// row of records (a buffer store there is dropped by the range check).
+constexpr int kBufferDword3 = 0x00020000;
+constexpr uint32_t kDropOffset = 0x80000000u;
 static_assert(4 + kCandCap / 2 <= kRecTailWords && kRecWords * 4 % 128 == 0, "record layout");
 constexpr int kSamplePagesPerWave = 16;                       // the first pages of each wave ...
 constexpr int kBlockSample = kScoreWaves * kSamplePagesPerWave * kPage;   // ... 1024 tokens per head
@@ -433,7 +437,7 @@ __global__ __launch_bounds__(kScoreWaves * 64, 2) void score_kernel(
 #pragma unroll
     for (int su = 0; su < kSamplePagesPerWave; ++su)
         if (p_begin + su < p_end) append_page(skey[su], su);
-    auto flush_slot = [&]() {
+    auto flush_slot = [&]() __attribute__((always_inline)) {
         // this wave's slot: per head one record (count, bound, largest key, then the
         // candidates in token order).  Head lane (col, quad) places its own entries:
         // the e-th set bit of its mask is the token of its e-th entry, which goes to
@@ -502,22 +506,33 @@ __global__ __launch_bounds__(kScoreWaves * 64, 2) void score_kernel(
         for (int q2 = 0; q2 < 4; ++q2) hm = max(hm, (uint32_t)__shfl((int)kmax, col + 16 * q2, 64));
         if (head_lane && quad == 0) *(u32x4 *)tail = u32x4{ovf ? kCandOverflow : total, lo, hm, 0u};
         wave_lds_sync();
-        // 16 B per lane: lanes 0..47 the key lines, then lanes 0..31 the tail lines
-        for (int hh = 0; hh < heads_here; ++hh) {
+        // 16 B per lane: lanes 0..47 the key lines, lanes 0..31 the tail lines.  The
+        // stores go through a buffer resource over the head's records, and a lane with
+        // nothing to write aims past them, where the store is dropped: every wave issues
+        // the same 2 kHeadBlock stores, so the compiler's waits for the next slot's
+        // loads (issued before them) need not wait for the stores as well.
+        const uint32_t row_bytes = (uint32_t)slots * kRecWords * 4u;
+        const uint32_t at = (uint32_t)slot * kRecWords * 4u + 16u * lane;
+#pragma unroll
+        for (int hh = 0; hh < kHeadBlock; ++hh) {
             const uint32_t tot = (uint32_t)__shfl((int)(ovf ? 0u : total), hh, 64);
-            u32x4 *rec = (u32x4 *)(cand_rec + (((int64_t)b * num_q_heads + h0 + hh) * slots + slot) * kRecWords);
-            const int key_chunks = (int)((tot + 31u) / 32u) * 8;                  // whole lines of keys
-            const int tail_chunks = (int)((4u + (tot + 1u) / 2u + 31u) / 32u) * 8; // header + positions
-            if (lane < key_chunks) rec[lane] = ((const u32x4 *)(out_key + hh * kCandCap))[lane];
-            if (lane < tail_chunks)
-                rec[kCandCap / 4 + lane] = ((const u32x4 *)(out_tail + hh * kRecTailWords))[lane];
+            const bool live = hh < heads_here;
+            const int64_t row_h = (int64_t)b * num_q_heads + h0 + min(hh, heads_here - 1);
+            const __amdgpu_buffer_rsrc_t rsrc =
+                __builtin_amdgcn_make_buffer_rsrc(cand_rec + row_h * slots * kRecWords, 0, (int)row_bytes, kBufferDword3);
+            const int key_chunks = live ? (int)((tot + 31u) / 32u) * 8 : 0;                  // whole lines of keys
+            const int tail_chunks = live ? (int)((4u + (tot + 1u) / 2u + 31u) / 32u) * 8 : 0; // header + positions
+            const u32x4 kv = ((const u32x4 *)(out_key + hh * kCandCap))[min(lane, kCandCap / 4 - 1)];
+            const u32x4 tv = ((const u32x4 *)(out_tail + hh * kRecTailWords))[min(lane, kRecTailWords / 4 - 1)];
+            __builtin_amdgcn_raw_buffer_store_b128(kv, rsrc, lane < key_chunks ? at : kDropOffset, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b128(tv, rsrc, lane < tail_chunks ? at + kCandCap * 4 : kDropOffset, 0, 0);
         }
     };
     // the main phase of slot S: its pages after the sample (slot 0) or all of them,
     // fully unrolled: straight-line code lets the compiler wait for exactly the group it
     // stages, with the next groups in flight.  The last groups of a slot put the
     // next slot's first pages in flight, so the flush overlaps their loads.
-    auto run_slot = [&](auto S) -> bool {
+    auto run_slot = [&](auto S) __attribute__((always_inline)) -> bool {
         constexpr int sl = decltype(S)::value;
         if constexpr (sl > 0) {
             p_begin = slot_begin(sl);
