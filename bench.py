@@ -300,7 +300,7 @@ def main():
     step_bytes = b_index + b_attend
     value = args.steps / wall
     traffic = read_traffic()
-    roofline = {"bound": "hbm", "kernel": "index_topk (sample_kernel + score_kernel + select_kernel)",
+    roofline = {"bound": "hbm", "kernel": "index_topk (score_kernel + select_kernel)",
                 "achieved": b_index / mi / 1e9, "peak": PEAK_HBM_BPS / 1e9, "unit": "GB/s",
                 "frac": b_index / mi / PEAK_HBM_BPS, "traffic": traffic,
                 "algorithmic_bytes_per_launch": b_index, "avg_launch_us": mi * 1e6}
