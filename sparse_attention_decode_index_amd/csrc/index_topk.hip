@@ -62,6 +62,7 @@ constexpr int kCandCap = 192;                                 // candidates kept
 constexpr int kSubCap = kCandCap / 4;                         // ... as 4 lane lists (one per quad) of 48
 constexpr int kSubStride = kSubCap + 1;                       // padded: lists start in different banks
 constexpr uint32_t kCandOverflow = 0xFFFFFFFFu;               // slot count of an overflowed list
+constexpr double kSlotExpectMax = 120.0;                      // larger expected slot counts: all-keys mode
 // A slot's record for one head, 1280 B (ten 128-byte lines): 32-bit keys [0, 192),
 // then the tail: count, bound, largest key, 0, and the 16-bit positions (token - slot
 // start) in token order.
@@ -211,12 +212,12 @@ __device__ __forceinline__ void threshold_bin_wave(const uint32_t *hist, int nbi
 // ---- 1. score pass -----------------------------------------------------------------------
 
 // grid (ceil(n_max / 2048), kv_heads * head_blocks, batch); 256 threads.
-template <int kSlots>
+template <int kSlots, bool kAllKeys>
 __global__ __launch_bounds__(kScoreWaves * 64, 2) void score_kernel(
     const uint16_t *__restrict__ kc, const int32_t *__restrict__ page_table,
     const int32_t *__restrict__ seq_lens, const uint16_t *__restrict__ q, const int32_t *__restrict__ k_per_seq,
     int num_q_heads, int num_kv_heads, int group, int head_blocks, int max_pages, int k_max,
-    uint32_t *__restrict__ cand_rec, int slots)
+    uint32_t *__restrict__ cand_rec, int slots, uint32_t *__restrict__ keys32, int64_t key_stride)
 {
     __shared__ int32_t pt_lds[kSlots * kScoreWaves * kScorePagesPerWave];
     __shared__ __attribute__((aligned(16))) unsigned char stage_all[kScoreWaves * kScoreUnroll * kStagePage];
@@ -319,7 +320,19 @@ __global__ __launch_bounds__(kScoreWaves * 64, 2) void score_kernel(
     // each entry's token from the mask, merges the 4 lists of a head into token order
     // and turns scores into keys.  Inside the head lanes it is branch-free: every score
     // is written, a rejected one into the lane's own pad slot, which is never read.
+    // (all-keys mode: every key goes to its head's key row; one buffer store per page,
+    // dropped for the lanes that carry no head)
+    const __amdgpu_buffer_rsrc_t key_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        keys32 + ((int64_t)b * num_q_heads + h0) * key_stride, 0, (int)(heads_here * key_stride * 4), kBufferDword3);
     auto append_page = [&](const uint32_t (&sc)[4], int po) {
+        if constexpr (kAllKeys) {
+            u32x4 kv;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) kv[i] = score_key(__uint_as_float(sc[i]));
+            const uint32_t off = (uint32_t)((col * key_stride + (p_begin + po) * kPage + 4 * quad) * 4);
+            __builtin_amdgcn_raw_buffer_store_b128(kv, key_rsrc, head_lane ? off : kDropOffset, 0, 0);
+            return;
+        }
         if (!head_lane) return;
         const int t0 = (p_begin + po) * kPage + 4 * quad;
 #pragma unroll
@@ -390,6 +403,7 @@ __global__ __launch_bounds__(kScoreWaves * 64, 2) void score_kernel(
         load_group(buf(G), p_begin + decltype(G)::value * kScoreUnroll, p_end);   // around loads in flight
         sched_fence();
     });
+    if constexpr (!kAllKeys) {
     static_for<0, kSampleGroups>([&](auto G) { sample_group(buf(G), decltype(G)::value * kScoreUnroll); });
     lds_barrier();
     // 2. per head hh (one wave each): its bound, the r-th largest sample code found by bisection,
@@ -437,7 +451,9 @@ __global__ __launch_bounds__(kScoreWaves * 64, 2) void score_kernel(
 #pragma unroll
     for (int su = 0; su < kSamplePagesPerWave; ++su)
         if (p_begin + su < p_end) append_page(skey[su], su);
+    }
     auto flush_slot = [&]() __attribute__((always_inline)) {
+        if constexpr (kAllKeys) return;                       // the keys are already out
         // this wave's slot: per head one record (count, bound, largest key, then the
         // candidates in token order).  Head lane (col, quad) places its own entries:
         // the e-th set bit of its mask is the token of its e-th entry, which goes to
@@ -544,7 +560,7 @@ __global__ __launch_bounds__(kScoreWaves * 64, 2) void score_kernel(
         }
         constexpr bool more = sl + 1 < kSlots;
         const int nb = more ? slot_begin(sl + 1) : 0, ne = more ? slot_end(sl + 1) : 0;
-        static_for<sl == 0 ? kSampleGroups : 0, kSlotGroups>([&](auto GI) {
+        static_for<sl == 0 && !kAllKeys ? kSampleGroups : 0, kSlotGroups>([&](auto GI) {
             constexpr int g = decltype(GI)::value;            // group in the slot
             constexpr int gn = g + kScoreBufs;                // the group its buffer loads next
             constexpr bool same = gn < kSlotGroups;
@@ -721,6 +737,7 @@ struct SelectArgs {
     const uint32_t *cand_rec;                                 // [row][slot] records of kRecWords
     int slots;                                                // slots per row
     int cap;                                                  // candidates the LDS holds (0: generic only)
+    int all_keys;                                             // the score pass wrote every key to keys32
     uint32_t *keys32;                                         // generic-path scratch, one row per (b, h)
     int64_t stride;
     int num_q_heads, num_kv_heads, group, max_pages, k_max;
@@ -777,6 +794,10 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a)
     int32_t *out = a.idx_out + bh * a.k_max;
     if (kk == n || kk == 0) {                                 // everything, or nothing
         for (int i = threadIdx.x; i < a.k_max; i += kSelThreads) out[i] = i < kk ? i : -1;
+        return;
+    }
+    if (a.all_keys) {
+        radix_select(RowKeys{a.keys32 + bh * a.stride}, n, kk, a.k_max, 0u, 32, 0u, hist, scratch, res, out);
         return;
     }
     bool generic = a.cap == 0;
@@ -943,6 +964,25 @@ hipError_t launch_index_topk(const IndexArgs &a, hipStream_t stream)
     uint32_t *keys32 = (uint32_t *)a.ws;
     uint32_t *cand_rec = keys32 + rows * stride;              // 512 B multiple: records start on lines
 
+    // LDS for the candidates.  A workgroup's bound is reached by about (n_w / 1024) r
+    // of its n_w tokens, r = mu + 6 sqrt(mu) + 8 and mu = 1024 k / n, so a row has
+    // about k + 6 sqrt(k n / 1024) + 8 n / 1024 candidates; the largest row bounds it
+    // (15% margin).  Rows beyond the capacity take the re-scoring path.
+    const double kd = a.k_max, nd = a.n_max;
+    const double expect = kd + 6.0 * std::sqrt(kd * nd / 1024.0) + 8.0 * nd / 1024.0;
+    // Beside the keys, the slot starts take (slots + 1) words and the walk starts one
+    // word per 64 keys.
+    const int cap_lds = ((int)(kSelDynMax / sizeof(uint32_t)) - (slots + 2)) * 64 / 65;
+    const int cap_want = (int)std::min<double>(1e9, std::ceil(1.15 * expect) + 256.0);
+    int cap = std::max(0, std::min(std::min(cap_want, kSelCapMax), cap_lds));
+    // A large k (or a row too long for the slot table) would overflow the slot lists or
+    // the LDS: then the score pass writes every key to the key rows and the select
+    // radix-selects over them (all-keys mode).  A slot expects r / 2 candidates.
+    const double mu = 1024.0 * kd / nd, r = mu + 6.0 * std::sqrt(mu) + 8.0;
+    const bool all_keys = cap_want > cap || r / 2.0 > kSlotExpectMax;
+    if (all_keys) cap = 0;
+    const size_t dyn = cap == 0 ? 0 : (size_t)(cap + slots + 1 + (cap + 63) / 64) * sizeof(uint32_t);
+
     // Two slots per wave when that gives every CU two workgroups for at most two rounds:
     // a workgroup's first flush then overlaps its second half's loads, and half as many
     // workgroups wait for their last stores.  Longer grids (many rounds of ragged rows)
@@ -951,27 +991,21 @@ hipError_t launch_index_topk(const IndexArgs &a, hipStream_t stream)
                             a.num_kv_heads * head_blocks * a.batch;
     const bool two = blocks2 >= 2 * kCUs && blocks2 <= 4 * kCUs;
     const int per_block = (two ? 2 : 1) * kScoreTokensPerBlock;
-    dim3 sgrid((a.n_max + per_block - 1) / per_block, a.num_kv_heads * head_blocks, a.batch);
-    if (two)
-        hipLaunchKernelGGL(score_kernel<2>, sgrid, dim3(kScoreWaves * 64), 0, stream, (const uint16_t *)a.k_cache,
+    const dim3 sgrid((a.n_max + per_block - 1) / per_block, a.num_kv_heads * head_blocks, a.batch);
+    auto launch_score = [&](auto kernel) {
+        hipLaunchKernelGGL(kernel, sgrid, dim3(kScoreWaves * 64), 0, stream, (const uint16_t *)a.k_cache,
                            a.page_table, a.seq_lens, (const uint16_t *)a.q, a.k_per_seq, a.num_q_heads,
-                           a.num_kv_heads, group, head_blocks, a.max_pages, a.k_max, cand_rec, slots);
-    else
-        hipLaunchKernelGGL(score_kernel<1>, sgrid, dim3(kScoreWaves * 64), 0, stream, (const uint16_t *)a.k_cache,
-                           a.page_table, a.seq_lens, (const uint16_t *)a.q, a.k_per_seq, a.num_q_heads,
-                           a.num_kv_heads, group, head_blocks, a.max_pages, a.k_max, cand_rec, slots);
+                           a.num_kv_heads, group, head_blocks, a.max_pages, a.k_max, cand_rec, slots, keys32,
+                           stride);
+    };
+    if (all_keys) {
+        if (two) launch_score(score_kernel<2, true>);
+        else launch_score(score_kernel<1, true>);
+    } else {
+        if (two) launch_score(score_kernel<2, false>);
+        else launch_score(score_kernel<1, false>);
+    }
 
-    // LDS for the candidates.  A workgroup's bound is reached by about (n_w / 1024) r
-    // of its n_w tokens, r = mu + 6 sqrt(mu) + 8 and mu = 1024 k / n, so a row has
-    // about k + 6 sqrt(k n / 1024) + 8 n / 1024 candidates; the largest row bounds it
-    // (15% margin).  Rows beyond the capacity take the re-scoring path.
-    const double kd = a.k_max, nd = a.n_max;
-    const double expect = kd + 6.0 * std::sqrt(kd * nd / 1024.0) + 8.0 * nd / 1024.0;
-    // Beside the keys, the slot starts take (slots + 1) words and the walk starts one
-    // word per 64 keys; rows so long that these crowd the keys out re-score (cap 0).
-    const int cap_lds = ((int)(kSelDynMax / sizeof(uint32_t)) - (slots + 2)) * 64 / 65;
-    const int cap = std::max(0, std::min((int)std::min<double>(kSelCapMax, std::ceil(1.15 * expect) + 256.0), cap_lds));
-    const size_t dyn = cap == 0 ? 0 : (size_t)(cap + slots + 1 + (cap + 63) / 64) * sizeof(uint32_t);
     if (dyn > 64 * 1024) {
         // raise the kernel's dynamic-LDS limit to the budget once (a function attribute,
         // not a stream operation)
@@ -984,7 +1018,7 @@ hipError_t launch_index_topk(const IndexArgs &a, hipStream_t stream)
         }
     }
     SelectArgs s{(const uint16_t *)a.k_cache, a.page_table, a.seq_lens, a.k_per_seq, (const uint16_t *)a.q,
-                 cand_rec, slots, cap, keys32, stride, a.num_q_heads, a.num_kv_heads,
+                 cand_rec, slots, cap, all_keys ? 1 : 0, keys32, stride, a.num_q_heads, a.num_kv_heads,
                  group, a.max_pages, a.k_max, a.idx_out};
     hipLaunchKernelGGL(select_kernel, dim3(a.num_q_heads, a.batch), dim3(kSelThreads), dyn, stream, s);
     return hipGetLastError();

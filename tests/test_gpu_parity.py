@@ -296,8 +296,20 @@ def test_select_fallback_paths():
     case = random_case(rng, batch=2, hq=4, hkv=1, lens=[20000, 17000], integer=True, lo=-1, hi=1)
     dev = DeviceCase.of_tiny(case)
     cache = oracle.Cache(case.k_cache, case.v_cache, case.page_table, case.lens)
-    run_and_check(dev, cache, case.q, np.array([9000, 400], np.int32), 9000, strict=True, check_dense=False,
+    run_and_check(dev, cache, case.q, np.array([2000, 400], np.int32), 2000, strict=True, check_dense=False,
                   tag="fallback")
+
+
+@pytest.mark.parametrize("integer", [False, True], ids=["random", "integer-ties"])
+def test_large_k_all_keys(integer):
+    """k a large share of N (2x-3x sparsity): the score pass writes every key and the
+    select radix-selects over the key rows; exact, ties included on integer inputs."""
+    rng = np.random.default_rng(14)
+    case = random_case(rng, batch=2, hq=8, hkv=2, lens=[5000, 3333], integer=integer, lo=-2, hi=2)
+    dev = DeviceCase.of_tiny(case)
+    cache = oracle.Cache(case.k_cache, case.v_cache, case.page_table, case.lens)
+    run_and_check(dev, cache, case.q, np.array([2500, 1111], np.int32), 2500, strict=integer,
+                  check_dense=False, tag="all-keys")
 
 
 def test_select_sample_bound_too_high():
