@@ -62,7 +62,7 @@ constexpr int kCandCap = 192;                                 // candidates kept
 constexpr int kSubCap = kCandCap / 4;                         // ... as 4 lane lists (one per quad) of 48
 constexpr int kSubStride = kSubCap + 1;                       // padded: lists start in different banks
 constexpr uint32_t kCandOverflow = 0xFFFFFFFFu;               // slot count of an overflowed list
-constexpr double kSlotExpectMax = 120.0;                      // larger expected slot counts: all-keys mode
+constexpr double kSlotExpectMax = 64.0;                       // larger expected slot counts: all-keys mode
 // A slot's record for one head, 1280 B (ten 128-byte lines): 32-bit keys [0, 192),
 // then the tail: count, bound, largest key, 0, and the 16-bit positions (token - slot
 // start) in token order.
@@ -84,8 +84,8 @@ constexpr int kSelThreads = 512;
 constexpr int kSelWaves = kSelThreads / 64;
 constexpr int kSelPerThread = 8;
 constexpr int kSelTile = kSelThreads * kSelPerThread;
-constexpr int kSelCapMax = 16384;                             // candidates gathered into LDS
-constexpr int kSelDynMax = 96 * 1024;                         // dynamic LDS: candidate keys + slot starts
+constexpr int kSelCapMax = 32768;                             // candidates gathered into LDS
+constexpr int kSelDynMax = 136 * 1024;                        // dynamic LDS: candidate keys + slot starts
 
 // MFMA B operand for the q rows of a head block: lane (col, quad) holds head col's
 // dims 32 s + 8 quad .. +7 (zeros for heads past the block).
@@ -669,7 +669,7 @@ __device__ __forceinline__ bool radix_select(const Src &src, int n, int kk, int 
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const uint32_t d = v[e] - base;
-                    if (e < cnt && (hi == 32 || (d >> hi) == prefix))
+                    if (e < cnt && v[e] >= base && (hi == 32 || (d >> hi) == prefix))
                         atomicAdd(&hist[(d >> lo) & ((1u << w) - 1u)], 1u);
                 }
             }
@@ -804,12 +804,12 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a)
     uint32_t *ckey = dyn_lds, *first = dyn_lds + a.cap, *blk = first + a.slots + 1;
     const int nslots = (n + kWaveTokens - 1) / kWaveTokens;
     uint32_t total = 0;
-    if (threadIdx.x < 8) res[threadIdx.x] = threadIdx.x == 5 ? 0xFFFFFFFFu : 0u;
+    if (threadIdx.x < 8) res[threadIdx.x] = 0u;
     if (!generic) {
         // 1. slot counts -> first[i], the place of slot i's first candidate.  An
         //    overflowed slot sends the row to the generic path.
         int bad = 0;
-        uint32_t lo_min = 0xFFFFFFFFu, lo_max = 0u, hi_max = 0u;
+        uint32_t lo_max = 0u, hi_max = 0u;
         for (int i = threadIdx.x; i < kHistBins; i += kSelThreads) hist[i] = 0u;
         for (int base = 0; base < a.slots; base += kSelThreads) {
             // loaded for every allocated slot (no wait for seq_lens), used below nslots
@@ -821,7 +821,6 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a)
             const uint32_t c_raw = hdr.x, l = hdr.y, hv = hdr.z;
             uint32_t c = i < nslots ? c_raw : 0u;
             if (i < nslots) {
-                lo_min = min(lo_min, l);
                 lo_max = max(lo_max, l);
                 if (c != 0u && c != kCandOverflow) hi_max = max(hi_max, hv);
             }
@@ -838,12 +837,10 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a)
         generic = bad != 0 || total < (uint32_t)kk || total > (uint32_t)a.cap;
 #pragma unroll
         for (int m = 32; m >= 1; m >>= 1) {
-            lo_min = min(lo_min, (uint32_t)__shfl_xor((int)lo_min, m, 64));
             lo_max = max(lo_max, (uint32_t)__shfl_xor((int)lo_max, m, 64));
             hi_max = max(hi_max, (uint32_t)__shfl_xor((int)hi_max, m, 64));
         }
         if ((threadIdx.x & 63) == 0) {
-            atomicMin(&res[5], lo_min);
             atomicMax(&res[6], lo_max);
             atomicMax(&res[7], hi_max);
         }
@@ -855,12 +852,16 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a)
     }
     // 2. gather the candidate keys into LDS in token order, one thread per slot (its
     //    list in 16-byte pieces, all in flight), counting the first radix digit of
-    //    d = key - lo on the way: lo is the smallest bound, and the largest candidate
-    //    key gives the digits' span (bits)
-    const uint32_t lo = res[5], lo_max = res[6];
-    const int bits = 32 - __clz((int)(res[7] - lo));
+    //    d = key - lo on the way.  lo is the largest bound: a key below it can never be
+    //    selected (T must reach every bound), so such keys stay in place but take no
+    //    part in the digits; a workgroup that kept all its tokens (bound 0, a row's
+    //    short tail) then does not stretch the digits over the whole key range.  The
+    //    largest candidate key gives the digits' span (bits).
+    const uint32_t lo = res[6], lo_max = lo, hi_max = res[7];
+    const int bits = hi_max >= lo ? 32 - __clz((int)(hi_max - lo)) : 0;
     const int w0 = min(12, bits), sh0 = bits - w0;
     const uint32_t mask0 = (1u << w0) - 1u;
+    uint32_t eligible = 0;                                    // keys >= lo this thread gathered
     for (int i = threadIdx.x; i < nslots; i += kSelThreads) {
         const uint32_t p0 = first[i], c = first[i + 1] - p0;
         const uint32_t *keys = rec_row + (int64_t)i * kRecWords;
@@ -877,14 +878,24 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a)
                     if (j < c) {
                         const uint32_t key = k4[u][e];
                         ckey[p0 + j] = key;
-                        if (bits > 0) atomicAdd(&hist[((key - lo) >> sh0) & mask0], 1u);
+                        if (key >= lo) {
+                            ++eligible;
+                            if (bits > 0) atomicAdd(&hist[((key - lo) >> sh0) & mask0], 1u);
+                        }
                     }
                 }
             }
         }
     }
+    eligible = wave_total(eligible);
+    if ((threadIdx.x & 63) == 0) atomicAdd(&res[4], eligible);
     if (threadIdx.x == 0) { res[0] = 0u; res[1] = 0u; res[2] = 0u; }
     __syncthreads();
+    if (res[4] < (uint32_t)kk) {                              // fewer than k keys reach every bound
+        __syncthreads();
+        select_rescore_generic(a, bh, b, h, n, kk, hist, scratch, res, out);
+        return;
+    }
     // 3. the k-th key T and r, the number of keys equal to T to take (the first ones):
     //    the first digit's bin b0 holds it; if the whole bin is taken and its floor
     //    already reaches every bound, the bin floor is T with all ties; otherwise the
@@ -901,7 +912,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a)
         } else {
             for (uint32_t v = threadIdx.x; v < total; v += kSelThreads) {
                 const uint32_t key = ckey[v];
-                if (((key - lo) >> sh0) == b0) {
+                if (key >= lo && ((key - lo) >> sh0) == b0) {
                     const uint32_t at = atomicAdd(&res[2], 1u);
                     if (at < 64u) blist[at] = key;
                 }
@@ -977,7 +988,11 @@ hipError_t launch_index_topk(const IndexArgs &a, hipStream_t stream)
     int cap = std::max(0, std::min(std::min(cap_want, kSelCapMax), cap_lds));
     // A large k (or a row too long for the slot table) would overflow the slot lists or
     // the LDS: then the score pass writes every key to the key rows and the select
-    // radix-selects over them (all-keys mode).  A slot expects r / 2 candidates.
+    // radix-selects over them (all-keys mode).  A slot expects r / 2 candidates, a
+    // quarter of them in each 48-entry lane list; at 64 per slot (16 per list) even a
+    // workgroup bound three deviations low leaves an overflow (a whole-row re-score)
+    // more than six deviations away.  At k = N/8 on the 16 x 131072 sweep, 120 per slot
+    // overflowed a few rows per hundred steps.
     const double mu = 1024.0 * kd / nd, r = mu + 6.0 * std::sqrt(mu) + 8.0;
     const bool all_keys = cap_want > cap || r / 2.0 > kSlotExpectMax;
     if (all_keys) cap = 0;
