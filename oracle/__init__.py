@@ -22,6 +22,13 @@ sparse-attention survey blog):
   forms, the one-hot closed form and k = 1.
 * ``dense``   the same over every cached token: the dense mode of Fig. 1a.
   Pinned by the k = N invariant and the closed forms above.
+* ``quest_summaries`` / ``quest_bounds`` / ``quest_select``  Quest-style page
+  selection (the Sparse Frontier review: section 3.5 Table 1, section 7.1, Eq. 10):
+  per 16-token page the elementwise min and max of its keys, the bound
+  sum_d max(q_d min_d, q_d max_d), and the current page plus the m - 1 other pages
+  of highest bound.  Pinned by the box property of min/max, the bound dominating
+  every token score of its page (tight for constant pages, closed forms for
+  one-signed queries), brute force over page subsets, and m >= pages giving dense.
 """
 from __future__ import annotations
 
@@ -58,6 +65,9 @@ def _declare(lib):
     lib.oracle_topk.argtypes = [p, p, p, i32, i32, i64, i32, p, p]
     lib.oracle_attend.argtypes = [p, p, p, p, i32, i32, i32, p, i32, p, i32, f64, p]
     lib.oracle_dense.argtypes = [p, p, p, p, i32, i32, i32, p, i32, f64, p]
+    lib.oracle_quest_summaries.argtypes = [p, p, p, i32, i32, i32, p]
+    lib.oracle_quest_bounds.argtypes = [p, p, i32, i32, i32, p, i32, p]
+    lib.oracle_quest_select.argtypes = [p, p, p, i32, i32, i32, i32, p, p, p]
     return lib
 
 
@@ -161,3 +171,42 @@ def decode_step(cache: Cache, q, k_per_seq, k_max: int, scale: float = DEFAULT_S
     idx, kth = topk(s, cache.sl, k_per_seq, k_max, lib=lib)
     out = attend(cache, q, idx, scale, lib=lib)
     return idx, kth, s, out
+
+
+def quest_summaries(cache: Cache, lib=None) -> np.ndarray:
+    """Per logical page [B][max_pages][Hkv][2][128] fp64: [0] the min, [1] the max of the
+    page's cached key rows (NaN for pages past the sequence)."""
+    lib = lib or _load()
+    out = np.full((cache.batch, cache.max_pages, cache.num_kv_heads, 2, 128), np.nan)
+    lib.oracle_quest_summaries(cache.kp, cache.ptp, cache.slp, cache.batch, cache.num_kv_heads, cache.max_pages,
+                               out.ctypes.data_as(ctypes.c_void_p))
+    return out
+
+
+def quest_bounds(summ, seq_lens, q, lib=None) -> np.ndarray:
+    """U [B][Hq][max_pages] fp64, U = sum_d max(q_d min_d, q_d max_d) (NaN past the sequence)."""
+    lib = lib or _load()
+    sm, smp = _c(summ, np.float64)
+    sl, slp = _c(seq_lens, np.int32)
+    q, qp = _c(q, np.uint16)
+    B, max_pages, hkv = sm.shape[:3]
+    hq = q.shape[1]
+    out = np.full((B, hq, max_pages), np.nan)
+    lib.oracle_quest_bounds(smp, slp, B, hkv, max_pages, qp, hq, out.ctypes.data_as(ctypes.c_void_p))
+    return out
+
+
+def quest_select(u, seq_lens, m_per_seq, m_max: int, lib=None):
+    """(pages [B][Hq][m_max], tokens [B][Hq][16 m_max], threshold [B][Hq]): the current
+    page plus the m - 1 other pages of highest bound (lower page first on ties)."""
+    lib = lib or _load()
+    uu, up = _c(u, np.float64)
+    sl, slp = _c(seq_lens, np.int32)
+    mm, mmp = _c(m_per_seq, np.int32)
+    B, hq, max_pages = uu.shape
+    pages = np.empty((B, hq, m_max), dtype=np.int32)
+    toks = np.empty((B, hq, 16 * m_max), dtype=np.int32)
+    thr = np.empty((B, hq), dtype=np.float64)
+    lib.oracle_quest_select(up, slp, mmp, B, hq, max_pages, m_max, pages.ctypes.data_as(ctypes.c_void_p),
+                            toks.ctypes.data_as(ctypes.c_void_p), thr.ctypes.data_as(ctypes.c_void_p))
+    return pages, toks, thr

@@ -224,3 +224,113 @@ void oracle_dense(const uint16_t *k_cache, const uint16_t *v_cache, const int32_
         free(all);
     }
 }
+
+/*
+ * Quest-style page selection (the Sparse Frontier review: section 3.5, Table 1 --
+ * Quest works at decode time on pages with a uniform budget over a full cache;
+ * section 7.1 -- 16-token pages, each represented by the minimum and maximum of
+ * its keys, the most relevant pages chosen at every step, the page holding the
+ * current token always included; Eq. 10 -- the page representations are what the
+ * selection loads).
+ *
+ *  quest_summaries  for every logical page p < ceil(N_b / 16) of sequence b and kv
+ *                   head g: kmin_d and kmax_d over the page's cached rows (tokens
+ *                   j < N_b only).  out [B][max_pages][Hkv][2][128] fp64, [0] = min,
+ *                   [1] = max; pages past the sequence are left untouched.
+ *  quest_bounds     U[b,h,p] = sum_d max(q_d * kmin_d, q_d * kmax_d), the largest
+ *                   q.k that any key inside the page's min/max box can reach, so an
+ *                   upper bound on the score of every token of the page.  (The pages
+ *                   give the representation and "most relevant", not the score; this
+ *                   is the score that representation plainly supports.)
+ *  quest_select     per (b, h), with P = ceil(N_b / 16) pages and m' = min(m_b, P,
+ *                   m_max): the last page (the current token's) plus the m' - 1 other
+ *                   pages of highest bound, ties to the lower page.  pages_out
+ *                   [B][Hq][m_max] ascending then -1; tok_out [B][Hq][16 m_max] the
+ *                   tokens j < N_b of those pages ascending, then -1; thr_out [B][Hq]
+ *                   the bound of the last page taken by rank (+inf if none was).
+ */
+void oracle_quest_summaries(const uint16_t *k_cache, const int32_t *page_table, const int32_t *seq_lens,
+                            int32_t batch, int32_t num_kv_heads, int32_t max_pages, double *out)
+{
+    orc_cache c = {k_cache, 0, page_table, seq_lens, batch, num_kv_heads, max_pages};
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t bg = 0; bg < (int64_t)batch * num_kv_heads; ++bg) {
+        int b = (int)(bg / num_kv_heads), g = (int)(bg % num_kv_heads);
+        int64_t n = seq_lens[b], pages = (n + ORC_PAGE - 1) / ORC_PAGE;
+        for (int64_t p = 0; p < pages; ++p) {
+            double *mn = out + (((int64_t)b * max_pages + p) * num_kv_heads + g) * 2 * ORC_D;
+            double *mx = mn + ORC_D;
+            for (int d = 0; d < ORC_D; ++d) { mn[d] = INFINITY; mx[d] = -INFINITY; }
+            for (int64_t j = p * ORC_PAGE; j < n && j < (p + 1) * ORC_PAGE; ++j) {
+                const uint16_t *row = row_of(k_cache, &c, b, g, j);
+                for (int d = 0; d < ORC_D; ++d) {
+                    double v = bf16_value(row[d]);
+                    if (v < mn[d]) mn[d] = v;
+                    if (v > mx[d]) mx[d] = v;
+                }
+            }
+        }
+    }
+}
+
+/* U [B][Hq][max_pages] fp64 from summaries [B][max_pages][Hkv][2][128]; pages past
+ * the sequence are left untouched. */
+void oracle_quest_bounds(const double *summ, const int32_t *seq_lens, int32_t batch, int32_t num_kv_heads,
+                         int32_t max_pages, const uint16_t *q, int32_t num_q_heads, double *u_out)
+{
+    int32_t G = num_q_heads / num_kv_heads;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t bh = 0; bh < (int64_t)batch * num_q_heads; ++bh) {
+        int b = (int)(bh / num_q_heads), h = (int)(bh % num_q_heads), g = h / G;
+        int64_t pages = ((int64_t)seq_lens[b] + ORC_PAGE - 1) / ORC_PAGE;
+        const uint16_t *qrow = q + bh * ORC_D;
+        for (int64_t p = 0; p < pages; ++p) {
+            const double *mn = summ + (((int64_t)b * max_pages + p) * num_kv_heads + g) * 2 * ORC_D;
+            const double *mx = mn + ORC_D;
+            double u = 0.0;
+            for (int d = 0; d < ORC_D; ++d) {
+                double qd = bf16_value(qrow[d]);
+                double lo = qd * mn[d], hi = qd * mx[d];
+                u += lo > hi ? lo : hi;
+            }
+            u_out[bh * max_pages + p] = u;
+        }
+    }
+}
+
+void oracle_quest_select(const double *u, const int32_t *seq_lens, const int32_t *m_per_seq, int32_t batch,
+                         int32_t num_q_heads, int32_t max_pages, int32_t m_max, int32_t *pages_out,
+                         int32_t *tok_out, double *thr_out)
+{
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t bh = 0; bh < (int64_t)batch * num_q_heads; ++bh) {
+        int b = (int)(bh / num_q_heads);
+        int64_t n = seq_lens[b], P = (n + ORC_PAGE - 1) / ORC_PAGE;
+        int64_t m = m_per_seq[b];
+        if (m > P) m = P;
+        if (m > m_max) m = m_max;
+        if (m < 0) m = 0;
+        int32_t *prow = pages_out + bh * m_max;
+        int64_t taken = 0;
+        double thr = INFINITY;
+        if (m > 0) {
+            prow[taken++] = (int32_t)(P - 1);            /* the current token's page */
+            /* the other pages by bound descending, then page ascending */
+            scored_token *rest = (scored_token *)malloc((size_t)(P > 1 ? P - 1 : 1) * sizeof *rest);
+            for (int64_t p = 0; p < P - 1; ++p) { rest[p].s = u[bh * max_pages + p]; rest[p].j = p; }
+            qsort(rest, (size_t)(P - 1), sizeof *rest, by_score_then_index);
+            for (int64_t i = 0; i < m - 1; ++i) prow[taken++] = (int32_t)rest[i].j;
+            if (m >= 2) thr = rest[m - 2].s;
+            free(rest);
+        }
+        qsort(prow, (size_t)taken, sizeof *prow, by_index);
+        for (int64_t i = taken; i < m_max; ++i) prow[i] = -1;
+        int32_t *trow = tok_out + bh * (int64_t)m_max * ORC_PAGE;
+        int64_t t = 0;
+        for (int64_t i = 0; i < taken; ++i)
+            for (int64_t j = (int64_t)prow[i] * ORC_PAGE; j < n && j < ((int64_t)prow[i] + 1) * ORC_PAGE; ++j)
+                trow[t++] = (int32_t)j;
+        for (; t < (int64_t)m_max * ORC_PAGE; ++t) trow[t] = -1;
+        if (thr_out) thr_out[bh] = thr;
+    }
+}

@@ -13,7 +13,12 @@ None of them recomputes a result the way the oracle does:
            arithmetic; uniform values; uniform keys; a one-hot key closed form;
            k = 1 returning the argmax row exactly;
 * dense:   equal to attending over every index (k = N) and to the closed forms;
-* layout:  identical results under contiguous, shuffled and fragmented pages.
+* layout:  identical results under contiguous, shuffled and fragmented pages;
+* quest:   page min/max are attained bounds of the page's rows (box property); the
+           page bound dominates every token score of its page, is tight on constant
+           pages and has closed forms for one-signed queries; the page choice equals
+           brute force over page subsets that hold the current page; every page
+           selected gives dense attention.
 """
 from __future__ import annotations
 
@@ -299,8 +304,118 @@ def pin_layout_invariance(lib):
             assert np.array_equal(x, y)
 
 
+# ---------------------------------------------------------------------------- quest pages
+
+def _quest_case(rng, layout="fragmented"):
+    return random_case(rng, batch=4, hq=6, hkv=2, lens=[1, 16, 17, 61], layout=layout)
+
+
+def pin_quest_box(lib):
+    """min/max of a page: every cached row lies inside, each bound is attained."""
+    rng = np.random.default_rng(31)
+    case = _quest_case(rng)
+    sm = oracle.quest_summaries(_cache(case), lib=lib)
+    for b in range(case.batch):
+        n = int(case.lens[b])
+        pages = -(-n // 16)
+        assert np.all(np.isnan(sm[b, pages:]))
+        for p in range(pages):
+            for g in range(case.num_kv_heads):
+                rows = case.k_f[b][g][16 * p:min(n, 16 * p + 16)]
+                mn, mx = sm[b, p, g, 0], sm[b, p, g, 1]
+                assert np.all(rows >= mn) and np.all(rows <= mx)
+                assert np.all((rows == mn).any(axis=0)) and np.all((rows == mx).any(axis=0))
+
+
+def pin_quest_bound(lib):
+    """The bound dominates the page's token scores; tight on constant pages; one-signed
+    queries give sum q max (q >= 0) or sum q min (q <= 0)."""
+    rng = np.random.default_rng(32)
+    case = _quest_case(rng, layout="shuffled")
+    c = _cache(case)
+    u = oracle.quest_bounds(oracle.quest_summaries(c, lib=lib), c.sl, case.q, lib=lib)
+    s = oracle.scores(c, case.q, lib=lib)
+    for b in range(case.batch):
+        n = int(case.lens[b])
+        for h in range(case.num_q_heads):
+            for j in range(n):
+                assert s[b, h, j] <= u[b, h, j // 16] + 1e-9 * (1 + abs(u[b, h, j // 16]))
+    # constant pages: every row of a page equal -> the bound is that row's score
+    k = [np.repeat(bf16_round(rng.standard_normal((2, 3, 1, 128))), 16, axis=2).reshape(2, 48, 128)]
+    v = [bf16_round(rng.standard_normal((2, 48, 128)))]
+    q = bf16_round(rng.standard_normal((1, 4, 128)))
+    tc = TinyCase(k, v, q, layout="fragmented", seed=5)
+    tcc = _cache(tc)
+    u2 = oracle.quest_bounds(oracle.quest_summaries(tcc, lib=lib), tcc.sl, tc.q, lib=lib)
+    s2 = oracle.scores(tcc, tc.q, lib=lib)
+    assert np.allclose(u2[0, :, :3], s2[0, :, ::16], rtol=1e-13, atol=1e-12)
+    # one-signed queries
+    qp = np.abs(bf16_round(rng.standard_normal((1, 4, 128))))
+    for sign, col in ((1.0, 1), (-1.0, 0)):
+        qs = TinyCase(case.k_f[3:], case.v_f[3:], sign * qp, layout="contiguous")
+        qc = _cache(qs)
+        u3 = oracle.quest_bounds(oracle.quest_summaries(qc, lib=lib), qc.sl, qs.q, lib=lib)
+        rows = case.k_f[3]
+        for h in range(4):
+            for p in range(-(-int(qs.lens[0]) // 16)):
+                blk = rows[h // 2][16 * p:16 * p + 16]
+                ext = blk.max(axis=0) if col == 1 else blk.min(axis=0)
+                want = float(sum(Fraction(float(a)) * Fraction(float(x)) for a, x in zip(sign * qp[0, h], ext)))
+                assert abs(u3[0, h, p] - want) <= 1e-12 * (1 + abs(want))
+
+
+def _brute_force_pages(u, n, m):
+    """The pages of a sequence of n tokens chosen under budget m by brute force: the
+    current page plus the subset of the others whose every member beats every
+    non-member (bound desc, page asc)."""
+    P = -(-n // 16)
+    m = min(m, P)
+    if m <= 0:
+        return []
+    others = list(range(P - 1))
+    beats = lambda i, j: u[i] > u[j] or (u[i] == u[j] and i < j)
+    found = [set(c) for c in itertools.combinations(others, m - 1)
+             if all(beats(i, j) for i in c for j in others if j not in c)]
+    assert len(found) == 1
+    return sorted(found[0] | {P - 1})
+
+
+def pin_quest_select_bruteforce(lib):
+    rng = np.random.default_rng(33)
+    for trial in range(60):
+        B, hq = 3, 2
+        lens = rng.integers(1, 113, size=B).astype(np.int32)   # up to 8 pages
+        m = rng.integers(0, 10, size=B).astype(np.int32)
+        m_max = 6
+        u = rng.integers(-3, 4, size=(B, hq, 8)).astype(np.float64)   # many ties
+        pages, toks, thr = oracle.quest_select(u, lens, m, m_max, lib=lib)
+        for b in range(B):
+            for h in range(hq):
+                want = _brute_force_pages(u[b, h], int(lens[b]), min(int(m[b]), m_max))
+                assert pages[b, h].tolist() == want + [-1] * (m_max - len(want))
+                tk = [j for p in want for j in range(16 * p, min(int(lens[b]), 16 * p + 16))]
+                assert toks[b, h].tolist() == tk + [-1] * (16 * m_max - len(tk))
+                ranked = [p for p in want if p != -(-int(lens[b]) // 16) - 1]
+                if ranked:
+                    assert thr[b, h] == min(u[b, h, p] for p in ranked)
+                else:
+                    assert thr[b, h] == np.inf
+
+
+def pin_quest_all_pages_is_dense(lib):
+    rng = np.random.default_rng(34)
+    case = random_case(rng, batch=3, hq=4, hkv=2, lens=[5, 33, 64], layout="fragmented")
+    c = _cache(case)
+    u = oracle.quest_bounds(oracle.quest_summaries(c, lib=lib), c.sl, case.q, lib=lib)
+    _, toks, _ = oracle.quest_select(u, c.sl, np.array([4, 4, 4], np.int32), 4, lib=lib)
+    a = oracle.attend(c, case.q, toks, SCALE, lib=lib)
+    d = oracle.dense(c, case.q, SCALE, lib=lib)
+    assert np.allclose(a, d, rtol=1e-12, atol=1e-14)
+
+
 ALL_PINS = [
     pin_topk_bruteforce, pin_topk_rank_count, pin_scores_exact, pin_scores_integer,
     pin_shift_invariance, pin_attend_decimal, pin_uniform_values, pin_uniform_keys, pin_one_hot,
     pin_k1_argmax_row, pin_dense_is_attend_all, pin_layout_invariance,
+    pin_quest_box, pin_quest_bound, pin_quest_select_bruteforce, pin_quest_all_pages_is_dense,
 ]

@@ -43,6 +43,17 @@ MUTANTS = {
                                   "double w = 1.0 + scale * dot_q_k(qrow, row_of(c->k, c, b, g, sel[i])) - m;"),
     "dense skips the last token": ("for (int64_t j = 0; j < n; ++j) all[j] = (int32_t)j;\n        attend_one(&c, b, h / G, q + bh * ORC_D, all, n,",
                                    "for (int64_t j = 0; j < n; ++j) all[j] = (int32_t)j;\n        attend_one(&c, b, h / G, q + bh * ORC_D, all, n - 1,"),
+    "quest min and max swapped": ("if (v < mn[d]) mn[d] = v;", "if (v > mn[d]) mn[d] = v;"),
+    "quest bound takes the smaller product": ("u += lo > hi ? lo : hi;", "u += lo < hi ? lo : hi;"),
+    "quest summary reads one row past the sequence": (
+        "for (int64_t j = p * ORC_PAGE; j < n && j < (p + 1) * ORC_PAGE; ++j) {",
+        "for (int64_t j = p * ORC_PAGE; j <= n && j < (p + 1) * ORC_PAGE; ++j) {"),
+    "quest forces the first page instead of the current one": ("prow[taken++] = (int32_t)(P - 1);",
+                                                               "prow[taken++] = 0;"),
+    "quest tokens past the sequence": (
+        "j < n && j < ((int64_t)prow[i] + 1) * ORC_PAGE; ++j)", "j < ((int64_t)prow[i] + 1) * ORC_PAGE; ++j)"),
+    "quest bound drops the last channel": ("for (int d = 0; d < ORC_D; ++d) {\n                double qd",
+                                           "for (int d = 0; d < ORC_D - 1; ++d) {\n                double qd"),
     "k not clamped to k_max": ("if (kk > k_max) kk = k_max;\n        if (kk < 0) kk = 0;",
                                "if (kk > k_max) kk = k_max - 1;\n        if (kk < 0) kk = 0;"),
 }
