@@ -55,7 +55,7 @@ enum {
     SDI_OK = 0,
     SDI_ERR_NULL = -1,       /* a required pointer is NULL */
     SDI_ERR_SHAPE = -2,      /* head_dim != 128, page_size != 16, heads not a multiple, sizes < 1 ... */
-    SDI_ERR_K = -3,          /* k_max < 1 */
+    SDI_ERR_K = -3,          /* k_max < 1 (pages_max < 1 for the page selection) */
     SDI_ERR_WORKSPACE = -4,  /* workspace smaller than the *_workspace() size */
     SDI_ERR_HIP = -5         /* a kernel launch failed */
 };
@@ -129,6 +129,51 @@ SDI_API int dense_decode(const sdi_kv *kv, const void *q, int32_t num_q_heads, f
                  float *out, void *ws, size_t ws_bytes, void *stream);
 
 SDI_API size_t dense_decode_workspace(const sdi_kv *kv, int32_t num_q_heads);
+
+/*
+ * Quest-style page selection (the Sparse Frontier review: section 3.5, Table 1 --
+ * a decode-time method selecting 16-token pages under a uniform budget over the
+ * full cache; section 7.1 -- each page represented by the elementwise minimum and
+ * maximum of its keys, the most relevant pages chosen every step, the page holding
+ * the current token always included; Eq. 10 -- selection loads the page
+ * representations).
+ *
+ * sparse_decode_quest_summarize writes, for every page p < ceil(N_b / 16) of every
+ * sequence and every kv head, the min and the max of each of the 128 dims over the
+ * page's cached rows (tokens j < N_b):
+ *   summary  bf16 [num_pages][num_kv_heads][2][128] (min row, then max row), indexed
+ *            by physical page, sparse_decode_quest_summary_bytes() bytes, owned by
+ *            the caller; pages no sequence reaches are left untouched.
+ *   current_pages_only  nonzero: only each sequence's last page ceil(N_b / 16) - 1
+ *            (the page a decode step appends to), zero: every page.
+ * Reads k_cache only.
+ *
+ * sparse_decode_quest_select scores every page of (b, q head h) with the bound
+ * U = sum_d max(q_d min_d, q_d max_d) (fp32 accumulation of bf16 products; the
+ * largest q.k any key inside the page's box can reach) and keeps the current page
+ * plus the m' - 1 other pages of highest bound, ties to the lower page, where
+ * m' = min(pages_per_seq[b], ceil(N_b / 16), pages_max):
+ *   q              bf16 [batch][num_q_heads][128], as for the indexer.
+ *   summary        as written by sparse_decode_quest_summarize for the same cache.
+ *   pages_per_seq  int32 [batch] device: the page budget m_b.
+ *   idx_out        int32 [batch][num_q_heads][16 * pages_max]: entry 16 i + r is token
+ *                  16 p_i + r of the i-th selected page p_i (ascending), or -1 when
+ *                  that token is past N_b or there is no i-th page.  This is an index
+ *                  list for sparse_decode_attend with k_max = 16 * pages_max (and
+ *                  k_per_seq NULL).
+ *   ws             device workspace of sparse_decode_quest_select_workspace() bytes.
+ * pages_max < 1 returns SDI_ERR_K.
+ */
+SDI_API size_t sparse_decode_quest_summary_bytes(const sdi_kv *kv);
+
+SDI_API int sparse_decode_quest_summarize(const sdi_kv *kv, void *summary, int32_t current_pages_only,
+                                          void *stream);
+
+SDI_API int sparse_decode_quest_select(const sdi_kv *kv, const void *q, int32_t num_q_heads, const void *summary,
+                                       const int32_t *pages_per_seq, int32_t pages_max, int32_t *idx_out,
+                                       void *ws, size_t ws_bytes, void *stream);
+
+SDI_API size_t sparse_decode_quest_select_workspace(const sdi_kv *kv, int32_t num_q_heads, int32_t pages_max);
 
 /* Static description of a return code (never NULL). */
 SDI_API const char *sparse_decode_strerror(int code);

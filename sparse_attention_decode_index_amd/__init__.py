@@ -27,6 +27,8 @@ EXPORTS = (
     "sparse_decode_index_topk", "sparse_decode_index_topk_workspace",
     "sparse_decode_attend", "sparse_decode_attend_workspace",
     "dense_decode", "dense_decode_workspace", "sparse_decode_strerror",
+    "sparse_decode_quest_summary_bytes", "sparse_decode_quest_summarize",
+    "sparse_decode_quest_select", "sparse_decode_quest_select_workspace",
 )
 
 
@@ -72,6 +74,14 @@ def load_library(path: str = LIB_PATH):
     lib.dense_decode.restype = ctypes.c_int
     lib.dense_decode_workspace.argtypes = [kvp, i32]
     lib.dense_decode_workspace.restype = sz
+    lib.sparse_decode_quest_summary_bytes.argtypes = [kvp]
+    lib.sparse_decode_quest_summary_bytes.restype = sz
+    lib.sparse_decode_quest_summarize.argtypes = [kvp, p, i32, p]
+    lib.sparse_decode_quest_summarize.restype = ctypes.c_int
+    lib.sparse_decode_quest_select.argtypes = [kvp, p, i32, p, p, i32, p, p, sz, p]
+    lib.sparse_decode_quest_select.restype = ctypes.c_int
+    lib.sparse_decode_quest_select_workspace.argtypes = [kvp, i32, i32]
+    lib.sparse_decode_quest_select_workspace.restype = sz
     lib.sparse_decode_strerror.argtypes = [ctypes.c_int]
     lib.sparse_decode_strerror.restype = ctypes.c_char_p
     if path == LIB_PATH:
@@ -223,3 +233,42 @@ def decode_step(kv: PagedKV, q, k_per_seq, k_max: int, softmax_scale: float = DE
     """One sparse decode step: exact top-k, then attend over the selected rows."""
     idx = index_topk(kv, q, k_per_seq, k_max, idx_out=idx_out, workspace=index_ws, stream=stream)
     return idx, attend(kv, q, idx, k_per_seq, softmax_scale, out=out, workspace=attend_ws, stream=stream)
+
+
+def quest_summarize(kv: PagedKV, summary=None, current_pages_only: bool = False, stream=None):
+    """Page min/max key summaries, bf16 [num_pages][Hkv][2][128] (min row, max row).
+    With current_pages_only, only each sequence's last page is (re)written."""
+    import torch
+    s = kv.struct()
+    lib = load_library()
+    if summary is None:
+        summary = torch.empty((s.num_pages, s.num_kv_heads, 2, HEAD_DIM), dtype=torch.bfloat16,
+                              device=kv.k_cache.device)
+    if summary.numel() * summary.element_size() < lib.sparse_decode_quest_summary_bytes(ctypes.byref(s)):
+        raise ValueError("summary buffer too small")
+    rc = lib.sparse_decode_quest_summarize(ctypes.byref(s), _ptr(summary), 1 if current_pages_only else 0,
+                                           _stream(stream))
+    if rc != SDI_OK:
+        raise SparseDecodeError(rc, "sparse_decode_quest_summarize")
+    return summary
+
+
+def quest_select(kv: PagedKV, q, summary, pages_per_seq, pages_max: int, idx_out=None, workspace=None,
+                 stream=None):
+    """Current page plus the highest-bound pages per (b, query head): token indices
+    int32 [B][Hq][16 pages_max] (page by page, -1 past N_b or past the selection)."""
+    import torch
+    _check(q, "q", torch.bfloat16, 3)
+    _check(pages_per_seq, "pages_per_seq", torch.int32, 1)
+    B, hq, _ = q.shape
+    if idx_out is None:
+        idx_out = torch.empty((B, hq, 16 * pages_max), dtype=torch.int32, device=q.device)
+    s = kv.struct()
+    lib = load_library()
+    ws = _workspace(lib.sparse_decode_quest_select_workspace(ctypes.byref(s), hq, pages_max), q.device, workspace)
+    rc = lib.sparse_decode_quest_select(ctypes.byref(s), _ptr(q), hq, _ptr(summary), _ptr(pages_per_seq),
+                                        pages_max, _ptr(idx_out), _ptr(ws), ws.numel() * ws.element_size(),
+                                        _stream(stream))
+    if rc != SDI_OK:
+        raise SparseDecodeError(rc, "sparse_decode_quest_select")
+    return idx_out

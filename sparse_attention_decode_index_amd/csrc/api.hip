@@ -103,13 +103,53 @@ int dense_decode(const sdi_kv *kv, const void *q, int32_t num_q_heads, float sof
     return hip_status(sdi::launch_dense(a, (hipStream_t)stream));
 }
 
+size_t sparse_decode_quest_summary_bytes(const sdi_kv *kv)
+{
+    if (!kv || kv->num_pages < 1 || kv->num_kv_heads < 1) return 0;
+    return sdi::quest_summary_bytes(kv->num_pages, kv->num_kv_heads);
+}
+
+size_t sparse_decode_quest_select_workspace(const sdi_kv *kv, int32_t num_q_heads, int32_t pages_max)
+{
+    if (!kv || kv->batch < 1 || kv->max_pages_per_seq < 1 || num_q_heads < 1 || pages_max < 1) return 0;
+    return sdi::quest_select_workspace_bytes(kv->batch, num_q_heads, kv->max_pages_per_seq, pages_max);
+}
+
+int sparse_decode_quest_summarize(const sdi_kv *kv, void *summary, int32_t current_pages_only, void *stream)
+{
+    int rc = check_kv(kv, false);
+    if (rc) return rc;
+    if (!summary) return SDI_ERR_NULL;
+    sdi::QuestArgs a{kv->k_cache, kv->page_table, kv->seq_lens, kv->batch, kv->num_kv_heads,
+                     kv->max_pages_per_seq, kv->n_max, summary, nullptr, 0, nullptr, 0, nullptr, nullptr};
+    return hip_status(sdi::launch_quest_summary(a, current_pages_only ? 1 : 0, (hipStream_t)stream));
+}
+
+int sparse_decode_quest_select(const sdi_kv *kv, const void *q, int32_t num_q_heads, const void *summary,
+                               const int32_t *pages_per_seq, int32_t pages_max, int32_t *idx_out, void *ws,
+                               size_t ws_bytes, void *stream)
+{
+    int rc = check_kv(kv, false);
+    if (rc) return rc;
+    if (!q || !summary || !pages_per_seq || !idx_out) return SDI_ERR_NULL;
+    if ((rc = check_heads(kv, num_q_heads))) return rc;
+    if (pages_max < 1 || pages_max > INT_MAX / 16) return SDI_ERR_K;
+    const size_t need = sparse_decode_quest_select_workspace(kv, num_q_heads, pages_max);
+    if (!ws) return SDI_ERR_NULL;
+    if (ws_bytes < need) return SDI_ERR_WORKSPACE;
+    sdi::QuestArgs a{kv->k_cache, kv->page_table, kv->seq_lens, kv->batch, kv->num_kv_heads,
+                     kv->max_pages_per_seq, kv->n_max, summary, q, num_q_heads, pages_per_seq, pages_max, idx_out,
+                     ws};
+    return hip_status(sdi::launch_quest_select(a, (hipStream_t)stream));
+}
+
 const char *sparse_decode_strerror(int code)
 {
     switch (code) {
     case SDI_OK: return "ok";
     case SDI_ERR_NULL: return "a required pointer is NULL";
     case SDI_ERR_SHAPE: return "unsupported shape (head_dim must be 128, page_size 16, q heads a multiple of kv heads, sizes >= 1)";
-    case SDI_ERR_K: return "k_max must be at least 1";
+    case SDI_ERR_K: return "k_max (or pages_max) must be at least 1";
     case SDI_ERR_WORKSPACE: return "workspace smaller than the size the *_workspace() query returns";
     case SDI_ERR_HIP: return "a HIP kernel launch failed";
     default: return "unknown sparse_decode status";

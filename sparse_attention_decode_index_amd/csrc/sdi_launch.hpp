@@ -36,6 +36,19 @@ struct AttendArgs {
     void *ws;
 };
 
+struct QuestArgs {
+    const void *k_cache;
+    const int32_t *page_table, *seq_lens;
+    int batch, num_kv_heads, max_pages, n_max;
+    const void *summary;       // [num_pages][Hkv][2][128] bf16 (written by the summary launch)
+    const void *q;             // select only
+    int num_q_heads;
+    const int32_t *pages_per_seq;
+    int pages_max;
+    int32_t *idx_out;          // [B][Hq][16 pages_max]
+    void *ws;
+};
+
 size_t index_topk_key_stride(int n_max);
 size_t index_topk_workspace_bytes(int batch, int num_q_heads, int n_max);
 hipError_t launch_index_topk(const IndexArgs &a, hipStream_t stream);
@@ -47,6 +60,11 @@ hipError_t launch_attend(const AttendArgs &a, hipStream_t stream);
 hipError_t launch_merge(const float *part_ml, const float *part_acc, int splits, int per_chunk,
                         const int32_t *counts, int count_cap, int batch, int num_q_heads, float *out,
                         hipStream_t stream);
+
+size_t quest_summary_bytes(int num_pages, int num_kv_heads);
+size_t quest_select_workspace_bytes(int batch, int num_q_heads, int max_pages, int pages_max);
+hipError_t launch_quest_summary(const QuestArgs &a, int last_only, hipStream_t stream);
+hipError_t launch_quest_select(const QuestArgs &a, hipStream_t stream);
 
 int dense_splits(int n_max);
 size_t dense_workspace_bytes(int batch, int num_q_heads, int n_max);

@@ -49,3 +49,10 @@ class DeviceCase:
         out = sdi.dense(self.kv, self.q, scale)
         torch.cuda.synchronize()
         return out.cpu().numpy()
+
+    def quest(self, pages_per_seq, pages_max, current_pages_only=False, summary=None):
+        """(summary bf16 bits [num_pages][Hkv][2][128], token list [B][Hq][16 pages_max])."""
+        summary = sdi.quest_summarize(self.kv, summary, current_pages_only)
+        idx = sdi.quest_select(self.kv, self.q, summary, i32_tensor(pages_per_seq), pages_max)
+        torch.cuda.synchronize()
+        return summary, summary.view(torch.int16).cpu().numpy().view(np.uint16), idx.cpu().numpy()

@@ -128,6 +128,30 @@ def test_argument_errors(lib):
     assert call_dense(lib, k, nbytes=need - 1) == sdi.SDI_ERR_WORKSPACE
 
 
+def test_quest_sizes_and_errors(lib):
+    k = kv()
+    # summaries: min and max row (2 x 128 bf16) per (physical page, kv head)
+    assert lib.sparse_decode_quest_summary_bytes(ctypes.byref(k)) == 40 * 2 * 2 * 128 * 2
+    # select workspace per (b, q head): one key per page (page rows padded to 64), then the page list
+    assert lib.sparse_decode_quest_select_workspace(ctypes.byref(k), 8, 6) == 2 * 8 * (64 * 4 + 6 * 4)
+    assert lib.sparse_decode_quest_select_workspace(ctypes.byref(k), 8, 0) == 0
+    assert lib.sparse_decode_quest_summarize(None, FAKE, 0, None) == sdi.SDI_ERR_NULL
+    assert lib.sparse_decode_quest_summarize(ctypes.byref(k), None, 0, None) == sdi.SDI_ERR_NULL
+    assert lib.sparse_decode_quest_summarize(ctypes.byref(kv(head_dim=64)), FAKE, 0, None) == sdi.SDI_ERR_SHAPE
+
+    def sel(hq=8, q=FAKE, summ=FAKE, pps=FAKE, pmax=6, out=FAKE, ws=FAKE, nbytes=1 << 40):
+        return lib.sparse_decode_quest_select(ctypes.byref(k), q, hq, summ, pps, pmax, out, ws, nbytes, None)
+    assert sel(q=None) == sdi.SDI_ERR_NULL
+    assert sel(summ=None) == sdi.SDI_ERR_NULL
+    assert sel(pps=None) == sdi.SDI_ERR_NULL
+    assert sel(out=None) == sdi.SDI_ERR_NULL
+    assert sel(ws=None) == sdi.SDI_ERR_NULL
+    assert sel(hq=3) == sdi.SDI_ERR_SHAPE
+    assert sel(pmax=0) == sdi.SDI_ERR_K
+    need = lib.sparse_decode_quest_select_workspace(ctypes.byref(k), 8, 6)
+    assert sel(nbytes=need - 1) == sdi.SDI_ERR_WORKSPACE
+
+
 def test_missing_library_fails_loudly(tmp_path):
     with pytest.raises(ImportError):
         sdi.load_library(str(tmp_path / "libsparse_decode.so"))
