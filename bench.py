@@ -14,6 +14,7 @@ timed on the host as a reported baseline.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import json
 import math
 import os
@@ -43,6 +44,10 @@ def parse_args():
     ap.add_argument("--cold", action="store_true", help="also time each launch group after a 1 GiB cache flush")
     ap.add_argument("--mode", choices=("graph", "eager"), default="graph",
                     help="replay captured HIP graphs (default) or launch eagerly from Python")
+    ap.add_argument("--quest", action="store_true",
+                    help="also time the Quest-style page selection step (current-page summary update, page "
+                         "selection, attend over the pages' tokens) at the same token budget, with its recall "
+                         "of the exact top-k")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="after timing, copy a buffer of this many MiB 3 times (a plain device copy of known "
                          "size, the reference for scaling memory-traffic counters)")
@@ -110,6 +115,69 @@ def cpu_baseline(wl, target_s):
     return {"value": 1.0 / per_step, "unit": "decode steps/s", "cores": oracle.num_threads(), "kind": "oracle",
             "sample": f"{reps} x the oracle's decode step (fp64 scores, exact top-k, attend) on {nb} of "
                       f"{wl.batch} sequences ({total:.1f} s), scaled to the whole batch"}
+
+
+def quest_leg(sdi, wl, kv_full, step_args, timed_graph, per, reps, k_max, idx, out, ws_attend, dense_s):
+    """Quest-style step at the exact indexer's token budget: the current pages'
+    summaries refreshed, the page selection (m = ceil(k / 16) pages, current page
+    included), then the gather-attend over those pages' tokens.  Recall = share of
+    the exact top-k tokens (step 0) that the selected pages contain."""
+    import torch
+    dev = idx.device
+    B, hq = wl.batch, wl.num_q_heads
+    pages_max = (k_max + 15) // 16
+    pps = torch.from_numpy(np.full(B, pages_max, np.int32)).to(dev)
+    summary = sdi.quest_summarize(kv_full)                   # prefill: every page once
+    qidx = torch.empty((B, hq, 16 * pages_max), dtype=torch.int32, device=dev)
+    ws_q = torch.empty(max(1, sdi.load_library().sparse_decode_quest_select_workspace(
+        ctypes.byref(kv_full.struct()), hq, pages_max)), dtype=torch.uint8, device=dev)
+    ws_qa = torch.empty(max(1, sdi.attend_workspace_bytes(kv_full, hq, 16 * pages_max)), dtype=torch.uint8,
+                        device=dev)
+
+    def update(s):
+        kv, _, _ = step_args(s)
+        sdi.quest_summarize(kv, summary, current_pages_only=True, stream=torch.cuda.current_stream())
+
+    def select(s):
+        kv, q, _ = step_args(s)
+        sdi.quest_select(kv, q, summary, pps, pages_max, idx_out=qidx, workspace=ws_q,
+                         stream=torch.cuda.current_stream())
+
+    def attend(s):
+        kv, q, _ = step_args(s)
+        sdi.attend(kv, q, qidx, None, out=out, workspace=ws_qa, stream=torch.cuda.current_stream())
+
+    def step(s):
+        update(s)
+        select(s)
+        attend(s)
+
+    for s in range(3):
+        step(s)
+    torch.cuda.synchronize()
+    t_upd, _ = timed_graph(update, max(1, reps), per)
+    t_sel, _ = timed_graph(select, max(1, reps), per)
+    t_att, _ = timed_graph(attend, max(1, reps), per)
+    t_step, _ = timed_graph(step, max(1, reps), per)
+    # recall of the exact selection, step 0
+    kv, q, kps = step_args(0)
+    sdi.index_topk(kv, q, kps, k_max, idx_out=idx)
+    select(0)
+    torch.cuda.synchronize()
+    ex, qt = idx.cpu().numpy(), qidx.cpu().numpy()
+    rec = []
+    for b in range(B):
+        for h in range(hq):
+            e = ex[b, h][ex[b, h] >= 0]
+            if len(e):
+                rec.append(np.isin(e, qt[b, h]).mean())
+    res = {"pages": pages_max, "tokens": 16 * pages_max, "summary_update_us": t_upd * 1e6,
+           "select_us": t_sel * 1e6, "attend_us": t_att * 1e6, "step_us": t_step * 1e6,
+           "recall_of_exact_topk": float(np.mean(rec)),
+           "select_bytes_per_launch": int((wl.num_kv_heads * ((wl.seq_lens.astype(np.int64) + 15) // 16) * 512).sum())}
+    if dense_s is not None:
+        res["speedup_vs_dense"] = dense_s / t_step
+    return res
 
 
 def main():
@@ -273,6 +341,10 @@ def main():
             torch.cuda.synchronize()
             dense_s = float(np.mean([e[0].elapsed_time(e[1]) for e in dev_ev]) * 1e-3)
 
+    quest = None
+    if args.quest and args.mode == "graph":
+        quest = quest_leg(sdi, wl, kv_full, step_args, timed_graph, per, reps, k_max, idx, out, ws_attend, dense_s)
+
     cold = {}
     if args.cold:
         flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -325,6 +397,8 @@ def main():
                        "dense_GBps": b_dense / dense_s / 1e9, "dense_pct_of_peak": 100 * b_dense / dense_s / PEAK_HBM_BPS,
                        "speedup_vs_dense": dense_s / (wall / args.steps),
                        "attend_speedup_vs_dense": dense_s / ma})
+    if quest is not None:
+        result["quest"] = quest
     result.update(cold)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)      # the host copy is still at step 0

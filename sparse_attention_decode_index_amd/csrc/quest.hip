@@ -14,7 +14,7 @@
 //     page: lane (r, c) takes rows r, r + 4, r + 8, r + 12 and dims 8c .. 8c + 7,
 //     then the 4 row groups combine by lane shuffles.  Bounds of bf16 values are
 //     bf16 values, so the summaries are exact.
-//  2. quest_bound_kernel    per (b, kv head, 64 pages): U for the G query heads of
+//  2. quest_bound_kernel    per (b, kv head, 256 pages): U for the G query heads of
 //     the group from the two summary rows (16 lanes x 16 B each), written as
 //     order-preserving 32-bit keys, the current page's as the largest key.  A
 //     matrix-vector product per head with a per-head choice of row, so it runs on
@@ -29,7 +29,7 @@
 namespace sdi {
 
 constexpr int kQuestSumRows = 2 * kHeadDim;                   // min row + max row per (page, kv head)
-constexpr int kQuestBoundPages = 64;                          // pages per bound workgroup (16 per wave)
+constexpr int kQuestBoundPages = 256;                         // pages per bound workgroup (64 per wave)
 constexpr int kQuestHeads = 8;                                // query heads per bound workgroup
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
@@ -86,8 +86,10 @@ __global__ __launch_bounds__(256) void quest_summary_kernel(const uint16_t *__re
     }
 }
 
-// grid (ceil(max_pages / 64), Hkv * head_blocks, B); 256 threads.  Lane group grp of
-// a wave takes pages base + 4 i + grp, i = 0..3; lane c of the group dims 8c .. 8c + 7.
+// grid (ceil(max_pages / 256), Hkv * head_blocks, B); 256 threads.  Each wave takes 64
+// pages in 4 batches of 16 (the next batch's summary rows in flight while one is
+// scored); lane group grp of a batch takes pages base + 4 i + grp, i = 0..3, and lane
+// c of the group dims 8c .. 8c + 7.
 __global__ __launch_bounds__(256) void quest_bound_kernel(const uint16_t *__restrict__ summary,
                                                           const int32_t *__restrict__ page_table,
                                                           const int32_t *__restrict__ seq_lens,
@@ -104,20 +106,23 @@ __global__ __launch_bounds__(256) void quest_bound_kernel(const uint16_t *__rest
     const int pages = (n + kPage - 1) / kPage;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int grp = lane >> 4, c = lane & 15;
-    const int base = (int)blockIdx.x * kQuestBoundPages + wave * 16;
-    if (base >= pages) return;                                // wave-uniform
+    const int base0 = (int)blockIdx.x * kQuestBoundPages + wave * (kQuestBoundPages / 4);
+    if (base0 >= pages) return;                               // wave-uniform
+    const int32_t *pt = page_table + (int64_t)b * max_pages;
 
-    // the summary rows of this lane's 4 pages (clamped to a page of the row; unused past it)
-    u32x4 smin[4], smax[4];
-    int pg[4];
+    // summary rows of batch j (pages clamped to the row; those past it are not scored)
+    auto load_batch = [&](int j, u32x4 (&smin)[4], u32x4 (&smax)[4]) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        pg[i] = base + 4 * i + grp;
-        const int64_t phys = page_table[(int64_t)b * max_pages + min(pg[i], pages - 1)];
-        const uint16_t *row = summary + (phys * num_kv_heads + g) * kQuestSumRows + 8 * c;
-        smin[i] = *(const u32x4 *)row;
-        smax[i] = *(const u32x4 *)(row + kHeadDim);
-    }
+        for (int i = 0; i < 4; ++i) {
+            const int p = min(base0 + 16 * j + 4 * i + grp, pages - 1);
+            const int64_t phys = pt[p];
+            const uint16_t *row = summary + (phys * num_kv_heads + g) * kQuestSumRows + 8 * c;
+            smin[i] = *(const u32x4 *)row;
+            smax[i] = *(const u32x4 *)(row + kHeadDim);
+        }
+    };
+    u32x4 amin[4], amax[4], bmin[4], bmax[4];
+    load_batch(0, amin, amax);
     float qf[kQuestHeads][8];
 #pragma unroll
     for (int h = 0; h < kQuestHeads; ++h) {
@@ -125,27 +130,37 @@ __global__ __launch_bounds__(256) void quest_bound_kernel(const uint16_t *__rest
         if (h < heads_here) w = *(const u32x4 *)(q + ((int64_t)b * num_q_heads + h0 + h) * kHeadDim + 8 * c);
         unpack8(w, qf[h]);
     }
+    auto score_batch = [&](int j, const u32x4 (&smin)[4], const u32x4 (&smax)[4]) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        float lo[8], hi[8];
-        unpack8(smin[i], lo);
-        unpack8(smax[i], hi);
-        float mine = 0.f;                                     // head c's bound (lanes c < heads_here)
+        for (int i = 0; i < 4; ++i) {
+            const int p = base0 + 16 * j + 4 * i + grp;
+            float lo[8], hi[8];
+            unpack8(smin[i], lo);
+            unpack8(smax[i], hi);
+            float mine = 0.f;                                 // head c's bound (lanes c < heads_here)
 #pragma unroll
-        for (int h = 0; h < kQuestHeads; ++h) {
-            if (h < heads_here) {                            // uniform
-                float part = 0.f;
+            for (int h = 0; h < kQuestHeads; ++h) {
+                if (h < heads_here) {                        // uniform
+                    float part = 0.f;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) part = fmaf(qf[h][e], qf[h][e] >= 0.f ? hi[e] : lo[e], part);
-                part = row16_sum(part);
-                if (c == h) mine = part;
+                    for (int e = 0; e < 8; ++e) part = fmaf(qf[h][e], qf[h][e] >= 0.f ? hi[e] : lo[e], part);
+                    part = row16_sum(part);
+                    if (c == h) mine = part;
+                }
+            }
+            if (c < heads_here && p < pages) {
+                const uint32_t key = p == pages - 1 ? 0xFFFFFFFFu : score_key(mine);
+                keys[((int64_t)b * num_q_heads + h0 + c) * key_stride + p] = key;
             }
         }
-        if (c < heads_here && pg[i] < pages) {
-            const uint32_t key = pg[i] == pages - 1 ? 0xFFFFFFFFu : score_key(mine);
-            keys[((int64_t)b * num_q_heads + h0 + c) * key_stride + pg[i]] = key;
-        }
-    }
+    };
+    load_batch(1, bmin, bmax);
+    score_batch(0, amin, amax);
+    load_batch(2, amin, amax);
+    score_batch(1, bmin, bmax);
+    load_batch(3, bmin, bmax);
+    score_batch(2, amin, amax);
+    score_batch(3, bmin, bmax);
 }
 
 // grid (Hq, B); kSelThreads threads.
