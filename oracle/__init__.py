@@ -22,6 +22,12 @@ sparse-attention survey blog):
   forms, the one-hot closed form and k = 1.
 * ``dense``   the same over every cached token: the dense mode of Fig. 1a.
   Pinned by the k = N invariant and the closed forms above.
+* ``label_scores``  reduced-channel scores for a lightweight indexer (the paper's
+  Fig. 1a indexer; the German summary, section 3, costs one with Double Sparsity;
+  the Sparse Frontier review, section 3.2, approximate scores from a few key
+  dimensions): s~ = sum over a kv head's R listed channels of q_c K_c.  Selection
+  is ``topk`` on s~.  Pinned by equality with ``scores`` when the channels are all
+  128 (or the keys vanish off the listed channels) and by exact rationals.
 * ``quest_summaries`` / ``quest_bounds`` / ``quest_select``  Quest-style page
   selection (the Sparse Frontier review: section 3.5 Table 1, section 7.1, Eq. 10):
   per 16-token page the elementwise min and max of its keys, the bound
@@ -65,6 +71,7 @@ def _declare(lib):
     lib.oracle_topk.argtypes = [p, p, p, i32, i32, i64, i32, p, p]
     lib.oracle_attend.argtypes = [p, p, p, p, i32, i32, i32, p, i32, p, i32, f64, p]
     lib.oracle_dense.argtypes = [p, p, p, p, i32, i32, i32, p, i32, f64, p]
+    lib.oracle_label_scores.argtypes = [p, p, p, i32, i32, i32, p, i32, p, i32, i64, p]
     lib.oracle_quest_summaries.argtypes = [p, p, p, i32, i32, i32, p]
     lib.oracle_quest_bounds.argtypes = [p, p, i32, i32, i32, p, i32, p]
     lib.oracle_quest_select.argtypes = [p, p, p, i32, i32, i32, i32, p, p, p]
@@ -210,3 +217,17 @@ def quest_select(u, seq_lens, m_per_seq, m_max: int, lib=None):
     lib.oracle_quest_select(up, slp, mmp, B, hq, max_pages, m_max, pages.ctypes.data_as(ctypes.c_void_p),
                             toks.ctypes.data_as(ctypes.c_void_p), thr.ctypes.data_as(ctypes.c_void_p))
     return pages, toks, thr
+
+
+def label_scores(cache: Cache, q, channels, lib=None) -> np.ndarray:
+    """fp64 reduced-channel scores [B][Hq][n_max]: sum over channels[g] (int32 [Hkv][R])
+    of q_c K_c, in the listed order (NaN beyond each sequence's length)."""
+    lib = lib or _load()
+    q, qp = _c(q, np.uint16)
+    ch, chp = _c(channels, np.int32)
+    hq = q.shape[1]
+    n_max = int(cache.sl.max())
+    out = np.full((cache.batch, hq, n_max), np.nan)
+    lib.oracle_label_scores(cache.kp, cache.ptp, cache.slp, cache.batch, cache.num_kv_heads, cache.max_pages,
+                            qp, hq, chp, ch.shape[1], n_max, out.ctypes.data_as(ctypes.c_void_p))
+    return out

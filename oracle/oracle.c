@@ -334,3 +334,37 @@ void oracle_quest_select(const double *u, const int32_t *seq_lens, const int32_t
         if (thr_out) thr_out[bh] = thr;
     }
 }
+
+/*
+ * Reduced-channel ("label") scores for a lightweight indexer: the paper's Fig. 1a
+ * routes the sparse mode through a lightweight indexer that picks the k rows, and
+ * the German summary (section 3, indexer overhead) costs one with Double Sparsity;
+ * the Sparse Frontier review (section 3.2) describes the same idea as approximate
+ * attention scores from a few key dimensions.  With a fixed channel set C_g of R
+ * channels per kv head (chosen offline by calibration):
+ *     s~[b,h,j] = sum_{i<R} q[b,h,C_g[i]] * K[b,g,j,C_g[i]],   g = h / G,
+ * summed over i in the listed order.  The selection is then the exact top-k of s~
+ * (oracle_topk) and attention runs on the selected rows in full (oracle_attend).
+ * channels: int32 [Hkv][R]; scores_out [B][Hq][n_stride], entries j >= N_b untouched.
+ */
+void oracle_label_scores(const uint16_t *k_cache, const int32_t *page_table, const int32_t *seq_lens,
+                         int32_t batch, int32_t num_kv_heads, int32_t max_pages, const uint16_t *q,
+                         int32_t num_q_heads, const int32_t *channels, int32_t r, int64_t n_stride,
+                         double *scores_out)
+{
+    orc_cache c = {k_cache, 0, page_table, seq_lens, batch, num_kv_heads, max_pages};
+    int32_t G = num_q_heads / num_kv_heads;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t bh = 0; bh < (int64_t)batch * num_q_heads; ++bh) {
+        int b = (int)(bh / num_q_heads), h = (int)(bh % num_q_heads), g = h / G;
+        const int32_t *ch = channels + (int64_t)g * r;     /* this kv head's channel list */
+        const uint16_t *qrow = q + bh * ORC_D;
+        for (int64_t j = 0; j < seq_lens[b]; ++j) {
+            const uint16_t *krow = row_of(k_cache, &c, b, g, j);
+            double s = 0.0;
+            for (int i = 0; i < r; ++i)
+                s += bf16_value(qrow[ch[i]]) * bf16_value(krow[ch[i]]);
+            scores_out[bh * n_stride + j] = s;
+        }
+    }
+}

@@ -18,7 +18,9 @@ None of them recomputes a result the way the oracle does:
            page bound dominates every token score of its page, is tight on constant
            pages and has closed forms for one-signed queries; the page choice equals
            brute force over page subsets that hold the current page; every page
-           selected gives dense attention.
+           selected gives dense attention;
+* labels:  all channels (or keys vanishing off the channel set) give the full
+           scores bit for bit; exact rationals on a tiny case.
 """
 from __future__ import annotations
 
@@ -413,9 +415,39 @@ def pin_quest_all_pages_is_dense(lib):
     assert np.allclose(a, d, rtol=1e-12, atol=1e-14)
 
 
+# ---------------------------------------------------------------------------- label scores
+
+def pin_label_scores(lib):
+    """All 128 channels in order give the full scores bit for bit; keys that vanish off
+    a 16-channel set give the full scores too; exact rationals on a tiny case."""
+    rng = np.random.default_rng(35)
+    case = random_case(rng, batch=2, hq=4, hkv=2, lens=[9, 40], layout="fragmented")
+    c = _cache(case)
+    full = oracle.scores(c, case.q, lib=lib)
+    allch = np.tile(np.arange(128, dtype=np.int32), (2, 1))
+    assert np.array_equal(np.nan_to_num(oracle.label_scores(c, case.q, allch, lib=lib)), np.nan_to_num(full))
+    ch = np.stack([np.sort(rng.choice(128, 16, replace=False)) for _ in range(2)]).astype(np.int32)
+    k = [np.zeros_like(kf) for kf in case.k_f]
+    for b in range(2):
+        for g in range(2):
+            k[b][g][:, ch[g]] = case.k_f[b][g][:, ch[g]]
+    zc = TinyCase(k, case.v_f, case.q_f, layout="shuffled", seed=3)
+    zcc = _cache(zc)
+    assert np.array_equal(np.nan_to_num(oracle.label_scores(zcc, zc.q, ch, lib=lib)),
+                          np.nan_to_num(oracle.scores(zcc, zc.q, lib=lib)))
+    got = oracle.label_scores(c, case.q, ch, lib=lib)
+    for b in range(2):
+        for h in range(4):
+            g = h // 2
+            for j in range(int(case.lens[b])):
+                want = sum(Fraction(float(case.q_f[b, h, d])) * Fraction(float(case.k_f[b][g][j, d])) for d in ch[g])
+                assert abs(got[b, h, j] - float(want)) <= 1e-12 * (1 + abs(float(want)))
+
+
 ALL_PINS = [
     pin_topk_bruteforce, pin_topk_rank_count, pin_scores_exact, pin_scores_integer,
     pin_shift_invariance, pin_attend_decimal, pin_uniform_values, pin_uniform_keys, pin_one_hot,
     pin_k1_argmax_row, pin_dense_is_attend_all, pin_layout_invariance,
     pin_quest_box, pin_quest_bound, pin_quest_select_bruteforce, pin_quest_all_pages_is_dense,
+    pin_label_scores,
 ]

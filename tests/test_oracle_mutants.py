@@ -54,6 +54,10 @@ MUTANTS = {
         "j < n && j < ((int64_t)prow[i] + 1) * ORC_PAGE; ++j)", "j < ((int64_t)prow[i] + 1) * ORC_PAGE; ++j)"),
     "quest bound drops the last channel": ("for (int d = 0; d < ORC_D; ++d) {\n                double qd",
                                            "for (int d = 0; d < ORC_D - 1; ++d) {\n                double qd"),
+    "label key channel not mapped": ("bf16_value(qrow[ch[i]]) * bf16_value(krow[ch[i]]);",
+                                     "bf16_value(qrow[ch[i]]) * bf16_value(krow[i]);"),
+    "label skips the first channel": ("for (int i = 0; i < r; ++i)\n                s += bf16_value(qrow[ch[i]])",
+                                      "for (int i = 1; i < r; ++i)\n                s += bf16_value(qrow[ch[i]])"),
     "k not clamped to k_max": ("if (kk > k_max) kk = k_max;\n        if (kk < 0) kk = 0;",
                                "if (kk > k_max) kk = k_max - 1;\n        if (kk < 0) kk = 0;"),
 }
