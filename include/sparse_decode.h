@@ -131,6 +131,43 @@ SDI_API int dense_decode(const sdi_kv *kv, const void *q, int32_t num_q_heads, f
 SDI_API size_t dense_decode_workspace(const sdi_kv *kv, int32_t num_q_heads);
 
 /*
+ * Lightweight top-k indexer on reduced-channel "label" rows (the paper's Fig. 1a:
+ * the sparse mode routes through a lightweight indexer that picks the k rows; the
+ * German summary, section 3, costs such an indexer with Double Sparsity; the Sparse
+ * Frontier review, section 3.2: approximate attention scores from a few key
+ * dimensions).  Each kv head g has a fixed list of 16 channels C_g (chosen offline by
+ * calibration); the indexer ranks tokens by
+ *     s~_j = sum_{i<16} q[C_g[i]] * K_j[C_g[i]]
+ * (bf16 products, fp32 accumulation in list order) and keeps the k' = min(k_b, N_b,
+ * k_max) largest, lower index first on equal scores.  Attention then runs on the
+ * selected rows in full (sparse_decode_attend).
+ *
+ * sparse_decode_label_build gathers those channels of every cached key:
+ *   channels  int32 [num_kv_heads][16] device, values in [0, 128) (not validated).
+ *   labels    bf16 [num_pages][num_kv_heads][16][16] (16 rows of a page, 16 channels),
+ *             sparse_decode_label_bytes() bytes, owned by the caller; pages no sequence
+ *             reaches are left untouched.
+ *   current_pages_only  nonzero: only each sequence's last page (the one a decode step
+ *             appends to), zero: every page.
+ * Reads k_cache only.
+ *
+ * sparse_decode_label_index_topk reads the label rows (32 B per token and kv head,
+ * 1/8 of the K rows) instead of the keys:
+ *   q, k_per_seq, k_max, idx_out  as for sparse_decode_index_topk.
+ *   labels, channels  as written by / given to sparse_decode_label_build.
+ *   ws         device workspace of sparse_decode_index_topk_workspace() bytes.
+ */
+SDI_API size_t sparse_decode_label_bytes(const sdi_kv *kv);
+
+SDI_API int sparse_decode_label_build(const sdi_kv *kv, const int32_t *channels, void *labels,
+                                      int32_t current_pages_only, void *stream);
+
+SDI_API int sparse_decode_label_index_topk(const sdi_kv *kv, const void *q, int32_t num_q_heads,
+                                           const void *labels, const int32_t *channels, const int32_t *k_per_seq,
+                                           int32_t k_max, int32_t *idx_out, void *ws, size_t ws_bytes,
+                                           void *stream);
+
+/*
  * Quest-style page selection (the Sparse Frontier review: section 3.5, Table 1 --
  * a decode-time method selecting 16-token pages under a uniform budget over the
  * full cache; section 7.1 -- each page represented by the elementwise minimum and

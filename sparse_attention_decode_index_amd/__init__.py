@@ -29,6 +29,7 @@ EXPORTS = (
     "dense_decode", "dense_decode_workspace", "sparse_decode_strerror",
     "sparse_decode_quest_summary_bytes", "sparse_decode_quest_summarize",
     "sparse_decode_quest_select", "sparse_decode_quest_select_workspace",
+    "sparse_decode_label_bytes", "sparse_decode_label_build", "sparse_decode_label_index_topk",
 )
 
 
@@ -74,6 +75,12 @@ def load_library(path: str = LIB_PATH):
     lib.dense_decode.restype = ctypes.c_int
     lib.dense_decode_workspace.argtypes = [kvp, i32]
     lib.dense_decode_workspace.restype = sz
+    lib.sparse_decode_label_bytes.argtypes = [kvp]
+    lib.sparse_decode_label_bytes.restype = sz
+    lib.sparse_decode_label_build.argtypes = [kvp, p, p, i32, p]
+    lib.sparse_decode_label_build.restype = ctypes.c_int
+    lib.sparse_decode_label_index_topk.argtypes = [kvp, p, i32, p, p, p, i32, p, p, sz, p]
+    lib.sparse_decode_label_index_topk.restype = ctypes.c_int
     lib.sparse_decode_quest_summary_bytes.argtypes = [kvp]
     lib.sparse_decode_quest_summary_bytes.restype = sz
     lib.sparse_decode_quest_summarize.argtypes = [kvp, p, i32, p]
@@ -271,4 +278,43 @@ def quest_select(kv: PagedKV, q, summary, pages_per_seq, pages_max: int, idx_out
                                         _stream(stream))
     if rc != SDI_OK:
         raise SparseDecodeError(rc, "sparse_decode_quest_select")
+    return idx_out
+
+
+def label_build(kv: PagedKV, channels, labels=None, current_pages_only: bool = False, stream=None):
+    """Label rows bf16 [num_pages][Hkv][16][16]: channels (int32 [Hkv][16], device) of
+    every cached key row.  With current_pages_only, only each sequence's last page."""
+    import torch
+    _check(channels, "channels", torch.int32, 2)
+    s = kv.struct()
+    lib = load_library()
+    if labels is None:
+        labels = torch.empty((s.num_pages, s.num_kv_heads, 16, 16), dtype=torch.bfloat16, device=kv.k_cache.device)
+    if labels.numel() * labels.element_size() < lib.sparse_decode_label_bytes(ctypes.byref(s)):
+        raise ValueError("label buffer too small")
+    rc = lib.sparse_decode_label_build(ctypes.byref(s), _ptr(channels), _ptr(labels),
+                                       1 if current_pages_only else 0, _stream(stream))
+    if rc != SDI_OK:
+        raise SparseDecodeError(rc, "sparse_decode_label_build")
+    return labels
+
+
+def label_index_topk(kv: PagedKV, q, labels, channels, k_per_seq, k_max: int, idx_out=None, workspace=None,
+                     stream=None):
+    """Top-k per (b, query head) of the reduced-channel scores: int32 [B][Hq][k_max]."""
+    import torch
+    _check(q, "q", torch.bfloat16, 3)
+    _check(k_per_seq, "k_per_seq", torch.int32, 1)
+    _check(channels, "channels", torch.int32, 2)
+    B, hq, _ = q.shape
+    if idx_out is None:
+        idx_out = torch.empty((B, hq, k_max), dtype=torch.int32, device=q.device)
+    s = kv.struct()
+    lib = load_library()
+    ws = _workspace(lib.sparse_decode_index_topk_workspace(ctypes.byref(s), hq, k_max), q.device, workspace)
+    rc = lib.sparse_decode_label_index_topk(ctypes.byref(s), _ptr(q), hq, _ptr(labels), _ptr(channels),
+                                            _ptr(k_per_seq), k_max, _ptr(idx_out), _ptr(ws),
+                                            ws.numel() * ws.element_size(), _stream(stream))
+    if rc != SDI_OK:
+        raise SparseDecodeError(rc, "sparse_decode_label_index_topk")
     return idx_out

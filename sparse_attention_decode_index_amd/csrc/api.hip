@@ -103,6 +103,41 @@ int dense_decode(const sdi_kv *kv, const void *q, int32_t num_q_heads, float sof
     return hip_status(sdi::launch_dense(a, (hipStream_t)stream));
 }
 
+size_t sparse_decode_label_bytes(const sdi_kv *kv)
+{
+    if (!kv || kv->num_pages < 1 || kv->num_kv_heads < 1) return 0;
+    return sdi::label_bytes(kv->num_pages, kv->num_kv_heads);
+}
+
+int sparse_decode_label_build(const sdi_kv *kv, const int32_t *channels, void *labels, int32_t current_pages_only,
+                              void *stream)
+{
+    int rc = check_kv(kv, false);
+    if (rc) return rc;
+    if (!channels || !labels) return SDI_ERR_NULL;
+    sdi::LabelArgs a{kv->k_cache, kv->page_table, kv->seq_lens, kv->batch, kv->num_kv_heads, kv->max_pages_per_seq,
+                     kv->n_max, channels, labels, nullptr, 0, nullptr, 0, nullptr, nullptr};
+    return hip_status(sdi::launch_label_build(a, current_pages_only ? 1 : 0, (hipStream_t)stream));
+}
+
+int sparse_decode_label_index_topk(const sdi_kv *kv, const void *q, int32_t num_q_heads, const void *labels,
+                                   const int32_t *channels, const int32_t *k_per_seq, int32_t k_max,
+                                   int32_t *idx_out, void *ws, size_t ws_bytes, void *stream)
+{
+    int rc = check_kv(kv, false);
+    if (rc) return rc;
+    if (!q || !labels || !channels || !k_per_seq || !idx_out) return SDI_ERR_NULL;
+    if ((rc = check_heads(kv, num_q_heads))) return rc;
+    if (k_max < 1) return SDI_ERR_K;
+    const size_t need = sparse_decode_index_topk_workspace(kv, num_q_heads, k_max);
+    if (need > 0 && !ws) return SDI_ERR_NULL;
+    if (ws_bytes < need) return SDI_ERR_WORKSPACE;
+    sdi::LabelArgs a{kv->k_cache, kv->page_table, kv->seq_lens, kv->batch, kv->num_kv_heads, kv->max_pages_per_seq,
+                     kv->n_max, channels, const_cast<void *>(labels), q, num_q_heads, k_per_seq, k_max, idx_out,
+                     ws};
+    return hip_status(sdi::launch_label_index_topk(a, (hipStream_t)stream));
+}
+
 size_t sparse_decode_quest_summary_bytes(const sdi_kv *kv)
 {
     if (!kv || kv->num_pages < 1 || kv->num_kv_heads < 1) return 0;

@@ -39,6 +39,7 @@
 #include "sdi_device.hpp"
 #include "sdi_launch.hpp"
 #include "sdi_radix.hpp"
+#include "sdi_index.hpp"
 
 #include <atomic>
 #include <cmath>
@@ -46,34 +47,14 @@
 
 namespace sdi {
 
-constexpr int kHeadBlock = 8;                                 // query heads scored per workgroup
-constexpr int kCUs = 256;                                     // MI355X compute units
-
 // ---- score pass --------------------------------------------------------------------------
-constexpr int kScoreWaves = 4;                                // two workgroups per CU (LDS < 80 KB each)
-constexpr int kScorePagesPerWave = 32;
 constexpr int kScoreUnroll = 2;                               // pages per register buffer (a group)
 constexpr int kScoreBufs = 2;                                 // groups in flight per wave (3 measured no faster)
 constexpr int kSlotGroups = kScorePagesPerWave / kScoreUnroll;
-constexpr int kWaveTokens = kScorePagesPerWave * kPage;       // 512 tokens: one candidate slot
-constexpr int kScoreTokensPerBlock = kScoreWaves * kWaveTokens;
 constexpr int kStageRow = kRowBytes + 16;                     // padded LDS row: conflict-free both ways
 constexpr int kStagePage = kPage * kStageRow;                 // 4352 B
-constexpr int kCandCap = 192;                                 // candidates kept per (slot, head)
 constexpr int kSubCap = kCandCap / 4;                         // ... as 4 lane lists (one per quad) of 48
 constexpr int kSubStride = kSubCap + 1;                       // padded: lists start in different banks
-constexpr uint32_t kCandOverflow = 0xFFFFFFFFu;               // slot count of an overflowed list
-constexpr double kSlotExpectMax = 64.0;                       // larger expected slot counts: all-keys mode
-// A slot's record for one head, 1280 B (ten 128-byte lines): 32-bit keys [0, 192),
-// then the tail: count, bound, largest key, 0, and the 16-bit positions (token - slot
-// start) in token order.
-constexpr int kRecTailWords = 128;                            // 512 B: 4 header words + 192 positions
-constexpr int kRecWords = kCandCap + kRecTailWords;
-// Buffer resource word 3 for untyped 32-bit accesses on gfx9, and an offset past any
-// row of records (a buffer store there is dropped by the range check).
-constexpr int kBufferDword3 = 0x00020000;
-constexpr uint32_t kDropOffset = 0x80000000u;
-static_assert(4 + kCandCap / 2 <= kRecTailWords && kRecWords * 4 % 128 == 0, "record layout");
 constexpr int kSamplePagesPerWave = 16;                       // the first pages of each wave ...
 constexpr int kBlockSample = kScoreWaves * kSamplePagesPerWave * kPage;   // ... 1024 tokens per head
 constexpr int kSampleGroups = kSamplePagesPerWave / kScoreUnroll;
@@ -81,9 +62,6 @@ static_assert(kSampleGroups % 2 == 0 && kSamplePagesPerWave <= kScorePagesPerWav
 
 
 // ---- select ------------------------------------------------------------------------------
-constexpr int kSelCapMax = 32768;                             // candidates gathered into LDS
-constexpr int kSelDynMax = 136 * 1024;                        // dynamic LDS: candidate keys + slot starts
-
 // MFMA B operand for the q rows of a head block: lane (col, quad) holds head col's
 // dims 32 s + 8 quad .. +7 (zeros for heads past the block).
 __device__ __forceinline__ void load_q_operand(bf16x8 (&qb)[4], const uint16_t *__restrict__ q, int64_t row0,
@@ -136,12 +114,6 @@ __device__ __forceinline__ void static_for(F &&f)
     }
 }
 
-__device__ __forceinline__ void wave_lds_sync()
-{
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
 
 // Workgroup barrier that orders LDS only: outstanding global loads stay in flight
 // (a full __syncthreads also waits for every vector memory operation).
@@ -555,22 +527,9 @@ struct LdsCandidates {
     }
 };
 
-struct SelectArgs {
-    const uint16_t *kc;
-    const int32_t *page_table, *seq_lens, *k_per_seq;
-    const uint16_t *q;
-    const uint32_t *cand_rec;                                 // [row][slot] records of kRecWords
-    int slots;                                                // slots per row
-    int cap;                                                  // candidates the LDS holds (0: generic only)
-    int all_keys;                                             // the score pass wrote every key to keys32
-    uint32_t *keys32;                                         // generic-path scratch, one row per (b, h)
-    int64_t stride;
-    int num_q_heads, num_kv_heads, group, max_pages, k_max;
-    int32_t *idx_out;
-};
-
 // Generic path for one head: re-score every token to its full 32-bit key in the
-// workspace row, then radix-select over the keys.  Called by the whole workgroup.
+// workspace row (from the K rows, or from the label rows for the lightweight
+// indexer), then radix-select over the keys.  Called by the whole workgroup.
 __device__ __forceinline__ void select_rescore_generic(const SelectArgs &a, int64_t bh, int b, int h, int n, int kk,
                                                        uint32_t *hist, uint32_t *scratch, uint32_t *res,
                                                        int32_t *__restrict__ out)
@@ -581,6 +540,22 @@ __device__ __forceinline__ void select_rescore_generic(const SelectArgs &a, int6
     const int heads_here = min(kHeadBlock, a.group - hb * kHeadBlock);
     uint32_t *krow = a.keys32 + bh * a.stride;
     const int32_t *pt = a.page_table + (int64_t)b * a.max_pages;
+    if (a.labels) {                                           // lightweight indexer: label rows
+        const int32_t *ch = a.channels + g * kLabelDims;
+        const uint16_t *qrow = a.q + bh * kHeadDim;
+        float qc[kLabelDims];
+#pragma unroll
+        for (int i = 0; i < kLabelDims; ++i) qc[i] = __uint_as_float((uint32_t)qrow[ch[i]] << 16);
+        for (int tok = threadIdx.x; tok < n; tok += kSelThreads) {
+            const int64_t row = ((int64_t)pt[tok >> 4] * a.num_kv_heads + g) * kPage + (tok & 15);
+            const u32x4 *lr = (const u32x4 *)(a.labels + row * kLabelDims);
+            krow[tok] = score_key(label_score(qc, lr[0], lr[1]));
+        }
+        __threadfence_block();
+        __syncthreads();
+        radix_select(RowKeys{krow}, n, kk, a.k_max, 0u, 32, 0u, hist, scratch, res, out);
+        return;
+    }
     bf16x8 qb[4];
     load_q_operand(qb, a.q, (int64_t)b * a.num_q_heads + g * a.group + hb * kHeadBlock, heads_here, col, quad);
     for (int t0 = wave * 16; t0 < n; t0 += kSelWaves * 16) {
@@ -780,7 +755,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a)
 
 size_t index_topk_key_stride(int n_max) { return (size_t)((n_max + 127) / 128) * 128; }
 
-static int index_topk_slots(int n_max) { return (n_max + kWaveTokens - 1) / kWaveTokens; }
+int index_topk_slots(int n_max) { return (n_max + kWaveTokens - 1) / kWaveTokens; }
 
 size_t index_topk_workspace_bytes(int batch, int num_q_heads, int n_max)
 {
@@ -790,21 +765,13 @@ size_t index_topk_workspace_bytes(int batch, int num_q_heads, int n_max)
     return rows * (index_topk_key_stride(n_max) * sizeof(uint32_t) + slots * kRecWords * sizeof(uint32_t));
 }
 
-hipError_t launch_index_topk(const IndexArgs &a, hipStream_t stream)
+SelectPlan plan_select(int k_max, int n_max, int slots)
 {
-    const int group = a.num_q_heads / a.num_kv_heads;
-    const int head_blocks = (group + kHeadBlock - 1) / kHeadBlock;
-    const int64_t stride = (int64_t)index_topk_key_stride(a.n_max);
-    const int slots = index_topk_slots(a.n_max);
-    const size_t rows = (size_t)a.batch * a.num_q_heads;
-    uint32_t *keys32 = (uint32_t *)a.ws;
-    uint32_t *cand_rec = keys32 + rows * stride;              // 512 B multiple: records start on lines
-
     // LDS for the candidates.  A workgroup's bound is reached by about (n_w / 1024) r
     // of its n_w tokens, r = mu + 6 sqrt(mu) + 8 and mu = 1024 k / n, so a row has
     // about k + 6 sqrt(k n / 1024) + 8 n / 1024 candidates; the largest row bounds it
     // (15% margin).  Rows beyond the capacity take the re-scoring path.
-    const double kd = a.k_max, nd = a.n_max;
+    const double kd = k_max, nd = n_max;
     const double expect = kd + 6.0 * std::sqrt(kd * nd / 1024.0) + 8.0 * nd / 1024.0;
     // Beside the keys, the slot starts take (slots + 1) words and the walk starts one
     // word per 64 keys.
@@ -822,6 +789,36 @@ hipError_t launch_index_topk(const IndexArgs &a, hipStream_t stream)
     const bool all_keys = cap_want > cap || r / 2.0 > kSlotExpectMax;
     if (all_keys) cap = 0;
     const size_t dyn = cap == 0 ? 0 : (size_t)(cap + slots + 1 + (cap + 63) / 64) * sizeof(uint32_t);
+    return SelectPlan{cap, dyn, all_keys};
+}
+
+hipError_t launch_select(const SelectArgs &s, const SelectPlan &p, int batch, hipStream_t stream)
+{
+    if (p.dyn > 64 * 1024) {
+        // raise the kernel's dynamic-LDS limit to the budget once (a function attribute,
+        // not a stream operation)
+        static std::atomic<bool> raised{false};
+        if (!raised.load(std::memory_order_acquire)) {
+            const hipError_t e = hipFuncSetAttribute((const void *)select_kernel,
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, kSelDynMax);
+            if (e != hipSuccess) return e;
+            raised.store(true, std::memory_order_release);
+        }
+    }
+    hipLaunchKernelGGL(select_kernel, dim3(s.num_q_heads, batch), dim3(kSelThreads), p.dyn, stream, s);
+    return hipGetLastError();
+}
+
+hipError_t launch_index_topk(const IndexArgs &a, hipStream_t stream)
+{
+    const int group = a.num_q_heads / a.num_kv_heads;
+    const int head_blocks = (group + kHeadBlock - 1) / kHeadBlock;
+    const int64_t stride = (int64_t)index_topk_key_stride(a.n_max);
+    const int slots = index_topk_slots(a.n_max);
+    const size_t rows = (size_t)a.batch * a.num_q_heads;
+    uint32_t *keys32 = (uint32_t *)a.ws;
+    uint32_t *cand_rec = keys32 + rows * stride;              // 512 B multiple: records start on lines
+    const SelectPlan plan = plan_select(a.k_max, a.n_max, slots);
 
     // Two slots per wave when that gives every CU two workgroups for at most two rounds:
     // a workgroup's first flush then overlaps its second half's loads, and half as many
@@ -838,30 +835,17 @@ hipError_t launch_index_topk(const IndexArgs &a, hipStream_t stream)
                            a.num_kv_heads, group, head_blocks, a.max_pages, a.k_max, cand_rec, slots, keys32,
                            stride);
     };
-    if (all_keys) {
+    if (plan.all_keys) {
         if (two) launch_score(score_kernel<2, true>);
         else launch_score(score_kernel<1, true>);
     } else {
         if (two) launch_score(score_kernel<2, false>);
         else launch_score(score_kernel<1, false>);
     }
-
-    if (dyn > 64 * 1024) {
-        // raise the kernel's dynamic-LDS limit to the budget once (a function attribute,
-        // not a stream operation)
-        static std::atomic<bool> raised{false};
-        if (!raised.load(std::memory_order_acquire)) {
-            const hipError_t e = hipFuncSetAttribute((const void *)select_kernel,
-                                                     hipFuncAttributeMaxDynamicSharedMemorySize, kSelDynMax);
-            if (e != hipSuccess) return e;
-            raised.store(true, std::memory_order_release);
-        }
-    }
     SelectArgs s{(const uint16_t *)a.k_cache, a.page_table, a.seq_lens, a.k_per_seq, (const uint16_t *)a.q,
-                 cand_rec, slots, cap, all_keys ? 1 : 0, keys32, stride, a.num_q_heads, a.num_kv_heads,
-                 group, a.max_pages, a.k_max, a.idx_out};
-    hipLaunchKernelGGL(select_kernel, dim3(a.num_q_heads, a.batch), dim3(kSelThreads), dyn, stream, s);
-    return hipGetLastError();
+                 cand_rec, slots, plan.cap, plan.all_keys ? 1 : 0, keys32, stride, a.num_q_heads, a.num_kv_heads,
+                 group, a.max_pages, a.k_max, a.idx_out, nullptr, nullptr};
+    return launch_select(s, plan, a.batch, stream);
 }
 
 }  // namespace sdi

@@ -1,0 +1,234 @@
+// Lightweight (reduced-channel) top-k indexer for the decode step (gfx950).
+//
+// The paper's Fig. 1a routes the sparse decode mode through a lightweight indexer
+// that picks the k rows; the German summary (section 3, indexer overhead) costs such
+// an indexer with Double Sparsity, and the Sparse Frontier review (section 3.2)
+// describes the idea as approximate attention scores from a few key dimensions.
+// Here each kv head has a fixed list of kLabelDims = 16 channels (chosen offline by
+// calibration); the "label" rows hold those channels of every cached key, 32 B per
+// token instead of 256 B, and the indexer ranks tokens by
+//     s~_j = sum_{i<16} q[C_g[i]] * K_j[C_g[i]]   (fp32, channel order),
+// keeping the exact top-k of s~ (lower index first on equal scores).
+//
+//  1. label_build_kernel   per (page, kv head): gathers the 16 channels of its 16
+//     rows into the label cache [num_pages][Hkv][16][16] bf16 (all pages, or each
+//     sequence's current page after an append).
+//  2. label_score_kernel   per (b, kv head, 2048 tokens): all s~ of the workgroup's
+//     tokens for its q heads into LDS (16-byte label loads, all in flight), then per
+//     head the workgroup's bound (bisection on the top 16 key bits for the r-th
+//     largest of its own scores, r = mu + 6 sqrt(mu) + 8, mu = n_w k / N) and, per
+//     512-token slot, the candidate record (ballot compaction in token order) that
+//     the exact indexer's select_kernel reads.  Large k: every key to the key rows.
+//  3. select_kernel        shared with the exact indexer; its re-scoring fallback
+//     recomputes s~ from the label rows.
+#include "sdi_device.hpp"
+#include "sdi_index.hpp"
+#include "sdi_launch.hpp"
+#include "sdi_radix.hpp"
+
+namespace sdi {
+
+constexpr int kLabelRowElems = kLabelDims;                    // bf16 per label row
+constexpr int kLabelPageElems = kPage * kLabelDims;           // 512 B per (page, kv head)
+constexpr int kLblPerThread = kScoreTokensPerBlock / (kScoreWaves * 64);   // 8 tokens per thread
+
+// grid (ceil(pages / 4), Hkv, B) or (1, Hkv, B) for the current pages only; 256 threads,
+// one wave per page: lane (row, part) gathers channels 4 part .. 4 part + 3 of a row.
+__global__ __launch_bounds__(256) void label_build_kernel(const uint16_t *__restrict__ kc,
+                                                          const int32_t *__restrict__ page_table,
+                                                          const int32_t *__restrict__ seq_lens,
+                                                          const int32_t *__restrict__ channels, int num_kv_heads,
+                                                          int max_pages, int last_only, uint16_t *__restrict__ labels)
+{
+    const int b = blockIdx.z, g = blockIdx.y;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int pages = (seq_lens[b] + kPage - 1) / kPage;
+    const int p = last_only ? (wave == 0 ? pages - 1 : -1) : (int)blockIdx.x * 4 + wave;
+    if (p < 0 || p >= pages) return;                          // wave-uniform
+    const int64_t blk = (int64_t)page_table[(int64_t)b * max_pages + p] * num_kv_heads + g;
+    const int row = lane >> 2, part = lane & 3;
+    const uint16_t *src = kc + (blk * kPage + row) * kHeadDim;
+    const int32_t *ch = channels + g * kLabelDims + 4 * part;
+    uint32_t v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = src[ch[i]];
+    *(uint2 *)(labels + blk * kLabelPageElems + row * kLabelRowElems + 4 * part) =
+        uint2{v[0] | (v[1] << 16), v[2] | (v[3] << 16)};
+}
+
+// grid (ceil(n_max / 2048), Hkv * head_blocks, B); 256 threads, two workgroups per CU.
+template <bool kAllKeys>
+__global__ __launch_bounds__(kScoreWaves * 64, 2) void label_score_kernel(
+    const uint16_t *__restrict__ labels, const int32_t *__restrict__ page_table,
+    const int32_t *__restrict__ seq_lens, const uint16_t *__restrict__ q, const int32_t *__restrict__ k_per_seq,
+    const int32_t *__restrict__ channels, int num_q_heads, int num_kv_heads, int group, int head_blocks,
+    int max_pages, int k_max, uint32_t *__restrict__ cand_rec, int slots, uint32_t *__restrict__ keys32,
+    int64_t key_stride)
+{
+    __shared__ uint32_t keys_lds[kHeadBlock][kScoreTokensPerBlock];          // 64 KB
+    __shared__ int32_t pt_lds[kScoreTokensPerBlock / kPage];
+    __shared__ __attribute__((aligned(16))) float qc_lds[kHeadBlock][kLabelDims];
+    __shared__ uint32_t lo_lds[kHeadBlock];
+    __shared__ __attribute__((aligned(16))) uint32_t img_all[kScoreWaves][kRecWords];
+    const int b = blockIdx.z;
+    const int g = blockIdx.y / head_blocks, hb = blockIdx.y - g * head_blocks;
+    const int n = seq_lens[b];
+    const int tok0 = blockIdx.x * kScoreTokensPerBlock;
+    if (tok0 >= n) return;                                    // whole block exits together
+    const int kk = min(min(k_per_seq[b], n), k_max);
+    const int heads_here = min(kHeadBlock, group - hb * kHeadBlock);
+    const int h0 = g * group + hb * kHeadBlock;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int n_wg = min(kScoreTokensPerBlock, n - tok0);     // the workgroup's tokens
+    {
+        const int i = threadIdx.x;
+        const int pages_seq = (n + kPage - 1) / kPage, p_base = tok0 / kPage;
+        if (i < kScoreTokensPerBlock / kPage && p_base + i < pages_seq)
+            pt_lds[i] = page_table[(int64_t)b * max_pages + p_base + i];
+        if (i < heads_here * kLabelDims) {
+            const int h = i / kLabelDims, c = i - h * kLabelDims;
+            qc_lds[h][c] = __uint_as_float(
+                (uint32_t)q[((int64_t)b * num_q_heads + h0 + h) * kHeadDim + channels[g * kLabelDims + c]] << 16);
+        }
+    }
+    __syncthreads();
+    // 1. s~ of every token for every head: thread t takes tokens t + 256 u
+    u32x4 w[kLblPerThread][2];
+#pragma unroll
+    for (int u = 0; u < kLblPerThread; ++u) {
+        const int tl = threadIdx.x + kScoreWaves * 64 * u;
+        w[u][0] = w[u][1] = u32x4{0u, 0u, 0u, 0u};
+        if (tl < n_wg) {
+            const int64_t row = ((int64_t)pt_lds[tl >> 4] * num_kv_heads + g) * kPage + (tl & 15);
+            const u32x4 *lr = (const u32x4 *)(labels + row * kLabelRowElems);
+            w[u][0] = lr[0];
+            w[u][1] = lr[1];
+        }
+    }
+    for (int h = 0; h < heads_here; ++h) {
+        float qc[kLabelDims];
+#pragma unroll
+        for (int i = 0; i < kLabelDims; ++i) qc[i] = qc_lds[h][i];
+#pragma unroll
+        for (int u = 0; u < kLblPerThread; ++u) {
+            const int tl = threadIdx.x + kScoreWaves * 64 * u;
+            keys_lds[h][tl] = tl < n_wg ? score_key(label_score(qc, w[u][0], w[u][1])) : 0u;
+        }
+    }
+    __syncthreads();
+    if constexpr (kAllKeys) {                                 // every key to the head's key row
+        for (int h = 0; h < heads_here; ++h) {
+            uint32_t *krow = keys32 + ((int64_t)b * num_q_heads + h0 + h) * key_stride + tok0;
+            for (int tl = threadIdx.x; tl < n_wg; tl += kScoreWaves * 64) krow[tl] = keys_lds[h][tl];
+        }
+        return;
+    }
+    // 2. per head (one wave each): the r-th largest code of the workgroup's own keys
+    for (int hh = wave; hh < heads_here; hh += kScoreWaves) {
+        uint32_t b_lo = 0xFFFFFFFFu;                          // k' = 0 or N: no candidates needed
+        if (kk > 0 && kk < n) {
+            const float mu = (float)n_wg * (float)kk / (float)n;
+            const uint32_t r = (uint32_t)ceilf(mu + 6.f * sqrtf(mu) + 8.f);
+            b_lo = 0u;                                        // a small workgroup keeps everything
+            if (r < (uint32_t)n_wg) {
+                uint32_t lo_c = 0, hi_c = 0x10000;            // count(code >= lo_c) >= r > count(code >= hi_c)
+                while (hi_c - lo_c > 1) {
+                    const uint32_t mid = (lo_c + hi_c) >> 1;
+                    uint32_t m = 0;
+                    for (int e = lane; e < kScoreTokensPerBlock; e += 64) m += (keys_lds[hh][e] >> 16) >= mid ? 1u : 0u;
+                    if (wave_total(m) >= r) lo_c = mid; else hi_c = mid;
+                }
+                b_lo = lo_c << 16;
+            }
+        }
+        if (lane == 0) lo_lds[hh] = b_lo;
+    }
+    __syncthreads();
+    // 3. the records: wave w takes the workgroup's slot w, head by head; candidates
+    //    (keys >= the bound) in token order by ballot, assembled in LDS, written out in
+    //    whole 128-byte lines through a buffer resource (dropped lanes aim past the row)
+    const int s_tok0 = tok0 + wave * kWaveTokens;
+    if (s_tok0 >= n) return;                                  // wave-uniform
+    const int slot = s_tok0 / kWaveTokens;
+    uint32_t *img = img_all[wave];
+    uint16_t *img_pos = (uint16_t *)(img + kCandCap + 4);
+    const uint32_t row_bytes = (uint32_t)slots * kRecWords * 4u;
+    const uint32_t at = (uint32_t)slot * kRecWords * 4u + 16u * lane;
+    for (int h = 0; h < heads_here; ++h) {
+        const uint32_t lo = lo_lds[h];
+        uint32_t cnt = 0, kmax = 0;
+#pragma unroll
+        for (int i = 0; i < kWaveTokens / 64; ++i) {
+            const int tl = wave * kWaveTokens + 64 * i + lane;
+            const uint32_t key = keys_lds[h][tl];
+            const bool take = tok0 + tl < n && key >= lo;
+            const uint64_t m = __ballot(take);
+            const uint32_t pos = cnt + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                                 __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+            if (take && pos < (uint32_t)kCandCap) {
+                img[pos] = key;
+                img_pos[pos] = (uint16_t)(64 * i + lane);
+            }
+            kmax = max(kmax, take ? key : 0u);
+            cnt += (uint32_t)__popcll(m);
+        }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o, 64));
+        const bool ovf = cnt > (uint32_t)kCandCap;
+        if (lane == 0) *(u32x4 *)(img + kCandCap) = u32x4{ovf ? kCandOverflow : cnt, lo, kmax, 0u};
+        wave_lds_sync();
+        const int64_t row_h = (int64_t)b * num_q_heads + h0 + h;
+        const __amdgpu_buffer_rsrc_t rsrc =
+            __builtin_amdgcn_make_buffer_rsrc(cand_rec + row_h * slots * kRecWords, 0, (int)row_bytes, kBufferDword3);
+        const uint32_t tot = ovf ? 0u : cnt;
+        const int key_chunks = (int)((tot + 31u) / 32u) * 8;
+        const int tail_chunks = (int)((4u + (tot + 1u) / 2u + 31u) / 32u) * 8;
+        const u32x4 kv = ((const u32x4 *)img)[min(lane, kCandCap / 4 - 1)];
+        const u32x4 tv = ((const u32x4 *)(img + kCandCap))[min(lane, kRecTailWords / 4 - 1)];
+        __builtin_amdgcn_raw_buffer_store_b128(kv, rsrc, lane < key_chunks ? at : kDropOffset, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(tv, rsrc, lane < tail_chunks ? at + kCandCap * 4 : kDropOffset, 0, 0);
+        wave_lds_sync();                                      // the image is free for the next head
+    }
+}
+
+// ---- host side ---------------------------------------------------------------------------
+
+size_t label_bytes(int num_pages, int num_kv_heads)
+{
+    return (size_t)num_pages * num_kv_heads * kLabelPageElems * sizeof(uint16_t);
+}
+
+hipError_t launch_label_build(const LabelArgs &a, int last_only, hipStream_t stream)
+{
+    const int bx = last_only ? 1 : (a.max_pages + 3) / 4;
+    hipLaunchKernelGGL(label_build_kernel, dim3(bx, a.num_kv_heads, a.batch), dim3(256), 0, stream,
+                       (const uint16_t *)a.k_cache, a.page_table, a.seq_lens, a.channels, a.num_kv_heads,
+                       a.max_pages, last_only, (uint16_t *)a.labels);
+    return hipGetLastError();
+}
+
+hipError_t launch_label_index_topk(const LabelArgs &a, hipStream_t stream)
+{
+    const int group = a.num_q_heads / a.num_kv_heads;
+    const int head_blocks = (group + kHeadBlock - 1) / kHeadBlock;
+    const int64_t stride = (int64_t)index_topk_key_stride(a.n_max);
+    const int slots = index_topk_slots(a.n_max);
+    uint32_t *keys32 = (uint32_t *)a.ws;
+    uint32_t *cand_rec = keys32 + (size_t)a.batch * a.num_q_heads * stride;
+    const SelectPlan plan = plan_select(a.k_max, a.n_max, slots);
+    const dim3 grid((a.n_max + kScoreTokensPerBlock - 1) / kScoreTokensPerBlock, a.num_kv_heads * head_blocks,
+                    a.batch);
+    auto launch_score = [&](auto kernel) {
+        hipLaunchKernelGGL(kernel, grid, dim3(kScoreWaves * 64), 0, stream, (const uint16_t *)a.labels,
+                           a.page_table, a.seq_lens, (const uint16_t *)a.q, a.k_per_seq, a.channels, a.num_q_heads,
+                           a.num_kv_heads, group, head_blocks, a.max_pages, a.k_max, cand_rec, slots, keys32, stride);
+    };
+    if (plan.all_keys) launch_score(label_score_kernel<true>);
+    else launch_score(label_score_kernel<false>);
+    SelectArgs s{(const uint16_t *)a.k_cache, a.page_table, a.seq_lens, a.k_per_seq, (const uint16_t *)a.q,
+                 cand_rec, slots, plan.cap, plan.all_keys ? 1 : 0, keys32, stride, a.num_q_heads, a.num_kv_heads,
+                 group, a.max_pages, a.k_max, a.idx_out, (const uint16_t *)a.labels, a.channels};
+    return launch_select(s, plan, a.batch, stream);
+}
+
+}  // namespace sdi

@@ -49,6 +49,20 @@ struct QuestArgs {
     void *ws;
 };
 
+struct LabelArgs {
+    const void *k_cache;
+    const int32_t *page_table, *seq_lens;
+    int batch, num_kv_heads, max_pages, n_max;
+    const int32_t *channels;   // [Hkv][16] device
+    void *labels;              // [num_pages][Hkv][16][16] bf16
+    const void *q;             // index only
+    int num_q_heads;
+    const int32_t *k_per_seq;
+    int k_max;
+    int32_t *idx_out;
+    void *ws;
+};
+
 size_t index_topk_key_stride(int n_max);
 size_t index_topk_workspace_bytes(int batch, int num_q_heads, int n_max);
 hipError_t launch_index_topk(const IndexArgs &a, hipStream_t stream);
@@ -60,6 +74,10 @@ hipError_t launch_attend(const AttendArgs &a, hipStream_t stream);
 hipError_t launch_merge(const float *part_ml, const float *part_acc, int splits, int per_chunk,
                         const int32_t *counts, int count_cap, int batch, int num_q_heads, float *out,
                         hipStream_t stream);
+
+size_t label_bytes(int num_pages, int num_kv_heads);
+hipError_t launch_label_build(const LabelArgs &a, int last_only, hipStream_t stream);
+hipError_t launch_label_index_topk(const LabelArgs &a, hipStream_t stream);
 
 size_t quest_summary_bytes(int num_pages, int num_kv_heads);
 size_t quest_select_workspace_bytes(int batch, int num_q_heads, int max_pages, int pages_max);

@@ -56,3 +56,11 @@ class DeviceCase:
         idx = sdi.quest_select(self.kv, self.q, summary, i32_tensor(pages_per_seq), pages_max)
         torch.cuda.synchronize()
         return summary, summary.view(torch.int16).cpu().numpy().view(np.uint16), idx.cpu().numpy()
+
+    def label_index(self, channels, k_per_seq, k_max, current_pages_only=False, labels=None):
+        """(label bits [num_pages][Hkv][16][16], indices [B][Hq][k_max])."""
+        ch = i32_tensor(channels)
+        labels = sdi.label_build(self.kv, ch, labels, current_pages_only)
+        idx = sdi.label_index_topk(self.kv, self.q, labels, ch, i32_tensor(k_per_seq), k_max)
+        torch.cuda.synchronize()
+        return labels.view(torch.int16).cpu().numpy().view(np.uint16), idx.cpu().numpy()

@@ -152,6 +152,23 @@ def test_quest_sizes_and_errors(lib):
     assert sel(nbytes=need - 1) == sdi.SDI_ERR_WORKSPACE
 
 
+def test_label_sizes_and_errors(lib):
+    k = kv()
+    assert lib.sparse_decode_label_bytes(ctypes.byref(k)) == 40 * 2 * 16 * 16 * 2   # 16 rows x 16 channels
+    assert lib.sparse_decode_label_build(ctypes.byref(k), None, FAKE, 0, None) == sdi.SDI_ERR_NULL
+    assert lib.sparse_decode_label_build(ctypes.byref(k), FAKE, None, 0, None) == sdi.SDI_ERR_NULL
+    assert lib.sparse_decode_label_build(ctypes.byref(kv(page_size=8)), FAKE, FAKE, 0, None) == sdi.SDI_ERR_SHAPE
+
+    def idx(hq=8, q=FAKE, lab=FAKE, ch=FAKE, kps=FAKE, k_max=5, out=FAKE, ws=FAKE, nbytes=1 << 40):
+        return lib.sparse_decode_label_index_topk(ctypes.byref(k), q, hq, lab, ch, kps, k_max, out, ws, nbytes, None)
+    for over in (dict(q=None), dict(lab=None), dict(ch=None), dict(kps=None), dict(out=None), dict(ws=None)):
+        assert idx(**over) == sdi.SDI_ERR_NULL
+    assert idx(hq=5) == sdi.SDI_ERR_SHAPE
+    assert idx(k_max=0) == sdi.SDI_ERR_K
+    need = lib.sparse_decode_index_topk_workspace(ctypes.byref(k), 8, 5)
+    assert idx(nbytes=need - 1) == sdi.SDI_ERR_WORKSPACE
+
+
 def test_missing_library_fails_loudly(tmp_path):
     with pytest.raises(ImportError):
         sdi.load_library(str(tmp_path / "libsparse_decode.so"))
