@@ -48,6 +48,9 @@ def parse_args():
                     help="also time the Quest-style page selection step (current-page summary update, page "
                          "selection, attend over the pages' tokens) at the same token budget, with its recall "
                          "of the exact top-k")
+    ap.add_argument("--labels", action="store_true",
+                    help="also time the lightweight indexer on 16-channel label rows (current-page label "
+                         "update, label index, attend), with its recall of the exact top-k")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="after timing, copy a buffer of this many MiB 3 times (a plain device copy of known "
                          "size, the reference for scaling memory-traffic counters)")
@@ -175,6 +178,76 @@ def quest_leg(sdi, wl, kv_full, step_args, timed_graph, per, reps, k_max, idx, o
            "select_us": t_sel * 1e6, "attend_us": t_att * 1e6, "step_us": t_step * 1e6,
            "recall_of_exact_topk": float(np.mean(rec)),
            "select_bytes_per_launch": int((wl.num_kv_heads * ((wl.seq_lens.astype(np.int64) + 15) // 16) * 512).sum())}
+    if dense_s is not None:
+        res["speedup_vs_dense"] = dense_s / t_step
+    return res
+
+
+def calibrate_channels(wl, r=16, sample=2048):
+    """Offline channel choice for the label indexer: per kv head the r channels of
+    largest mean |K| over the first `sample` tokens of sequence 0 (a calibration
+    sample, not the step's data)."""
+    vals = (wl.k_cache.astype(np.uint32) << 16).view(np.float32)
+    n = min(sample, int(wl.seq_lens[0]))
+    pages = wl.page_table[0, :-(-n // 16)]
+    ch = np.zeros((wl.num_kv_heads, r), np.int32)
+    for g in range(wl.num_kv_heads):
+        rows = vals[pages, g].reshape(-1, 128)[:n]
+        ch[g] = np.sort(np.argsort(-np.abs(rows).mean(axis=0), kind="stable")[:r])
+    return ch
+
+
+def labels_leg(sdi, wl, kv_full, step_args, timed_graph, per, reps, k_max, idx, out, ws_index, ws_attend,
+               dense_s):
+    """Lightweight-indexer step at the same k: the current pages' label rows refreshed,
+    the top-k of the 16-channel scores, then the gather-attend.  Recall = share of the
+    exact top-k tokens (step 0) that the label indexer also selects."""
+    import torch
+    dev = idx.device
+    ch = torch.from_numpy(calibrate_channels(wl)).to(dev)
+    labels = sdi.label_build(kv_full, ch)                    # prefill: every page once
+    lidx = torch.empty_like(idx)
+
+    def update(s):
+        kv, _, _ = step_args(s)
+        sdi.label_build(kv, ch, labels, current_pages_only=True, stream=torch.cuda.current_stream())
+
+    def index(s):
+        kv, q, kps = step_args(s)
+        sdi.label_index_topk(kv, q, labels, ch, kps, k_max, idx_out=lidx, workspace=ws_index,
+                             stream=torch.cuda.current_stream())
+
+    def attend(s):
+        kv, q, kps = step_args(s)
+        sdi.attend(kv, q, lidx, kps, out=out, workspace=ws_attend, stream=torch.cuda.current_stream())
+
+    def step(s):
+        update(s)
+        index(s)
+        attend(s)
+
+    for s in range(3):
+        step(s)
+    torch.cuda.synchronize()
+    t_upd, _ = timed_graph(update, max(1, reps), per)
+    t_idx, _ = timed_graph(index, max(1, reps), per)
+    t_att, _ = timed_graph(attend, max(1, reps), per)
+    t_step, _ = timed_graph(step, max(1, reps), per)
+    kv, q, kps = step_args(0)
+    sdi.index_topk(kv, q, kps, k_max, idx_out=idx)
+    index(0)
+    torch.cuda.synchronize()
+    ex, lt = idx.cpu().numpy(), lidx.cpu().numpy()
+    rec = []
+    for b in range(wl.batch):
+        for h in range(wl.num_q_heads):
+            e = ex[b, h][ex[b, h] >= 0]
+            if len(e):
+                rec.append(np.isin(e, lt[b, h]).mean())
+    n = wl.seq_lens.astype(np.int64)
+    res = {"channels": 16, "label_update_us": t_upd * 1e6, "index_us": t_idx * 1e6, "attend_us": t_att * 1e6,
+           "step_us": t_step * 1e6, "recall_of_exact_topk": float(np.mean(rec)),
+           "index_bytes_per_launch": int((wl.num_kv_heads * n * 32).sum())}
     if dense_s is not None:
         res["speedup_vs_dense"] = dense_s / t_step
     return res
@@ -345,6 +418,11 @@ def main():
     if args.quest and args.mode == "graph":
         quest = quest_leg(sdi, wl, kv_full, step_args, timed_graph, per, reps, k_max, idx, out, ws_attend, dense_s)
 
+    labels = None
+    if args.labels and args.mode == "graph":
+        labels = labels_leg(sdi, wl, kv_full, step_args, timed_graph, per, reps, k_max, idx, out, ws_index,
+                            ws_attend, dense_s)
+
     cold = {}
     if args.cold:
         flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -399,6 +477,8 @@ def main():
                        "attend_speedup_vs_dense": dense_s / ma})
     if quest is not None:
         result["quest"] = quest
+    if labels is not None:
+        result["labels"] = labels
     result.update(cold)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)      # the host copy is still at step 0

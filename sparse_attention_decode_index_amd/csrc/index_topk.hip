@@ -115,14 +115,6 @@ __device__ __forceinline__ void static_for(F &&f)
 }
 
 
-// Workgroup barrier that orders LDS only: outstanding global loads stay in flight
-// (a full __syncthreads also waits for every vector memory operation).
-__device__ __forceinline__ void lds_barrier()
-{
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
 
 // ---- 1. score pass -----------------------------------------------------------------------
 

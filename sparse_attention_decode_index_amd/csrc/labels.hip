@@ -13,12 +13,13 @@
 //  1. label_build_kernel   per (page, kv head): gathers the 16 channels of its 16
 //     rows into the label cache [num_pages][Hkv][16][16] bf16 (all pages, or each
 //     sequence's current page after an append).
-//  2. label_score_kernel   per (b, kv head, 2048 tokens): all s~ of the workgroup's
-//     tokens for its q heads into LDS (16-byte label loads, all in flight), then per
-//     head the workgroup's bound (bisection on the top 16 key bits for the r-th
-//     largest of its own scores, r = mu + 6 sqrt(mu) + 8, mu = n_w k / N) and, per
-//     512-token slot, the candidate record (ballot compaction in token order) that
-//     the exact indexer's select_kernel reads.  Large k: every key to the key rows.
+//  2. label_score_kernel   per (b, kv head, 2048 tokens): s~ of the workgroup's
+//     tokens for its q heads (16-byte label loads, all in flight; keys stay in the
+//     registers of the lane that scored them, their top 16 bits go to LDS), then per
+//     head the workgroup's bound (bisection on those codes for the r-th largest of its
+//     own scores, r = mu + 6 sqrt(mu) + 8, mu = n_w k / N) and, per 512-token slot,
+//     the candidate record (ballot placement in token order) that the exact
+//     indexer's select_kernel reads.  Large k: every key to the key rows.
 //  3. select_kernel        shared with the exact indexer; its re-scoring fallback
 //     recomputes s~ from the label rows.
 #include "sdi_device.hpp"
@@ -56,20 +57,22 @@ __global__ __launch_bounds__(256) void label_build_kernel(const uint16_t *__rest
         uint2{v[0] | (v[1] << 16), v[2] | (v[3] << 16)};
 }
 
-// grid (ceil(n_max / 2048), Hkv * head_blocks, B); 256 threads, two workgroups per CU.
+// grid (ceil(n_max / 2048), Hkv * head_blocks, B); 256 threads, three workgroups per CU.
+// Wave w owns the workgroup's slot w (tokens 512 w .. 512 w + 511), lane l its tokens
+// 512 w + 64 i + l, i = 0..7: it scores them, keeps their keys in registers for the
+// records, and shares only their 16-bit codes (for the workgroup's bound) in LDS.
 template <bool kAllKeys>
-__global__ __launch_bounds__(kScoreWaves * 64, 2) void label_score_kernel(
+__global__ __launch_bounds__(kScoreWaves * 64, 3) void label_score_kernel(
     const uint16_t *__restrict__ labels, const int32_t *__restrict__ page_table,
     const int32_t *__restrict__ seq_lens, const uint16_t *__restrict__ q, const int32_t *__restrict__ k_per_seq,
     const int32_t *__restrict__ channels, int num_q_heads, int num_kv_heads, int group, int head_blocks,
     int max_pages, int k_max, uint32_t *__restrict__ cand_rec, int slots, uint32_t *__restrict__ keys32,
     int64_t key_stride)
 {
-    __shared__ uint32_t keys_lds[kHeadBlock][kScoreTokensPerBlock];          // 64 KB
-    __shared__ int32_t pt_lds[kScoreTokensPerBlock / kPage];
+    constexpr int kPer = kWaveTokens / 64;                    // 8 tokens per lane
+    __shared__ __attribute__((aligned(16))) uint16_t codes[kHeadBlock][kScoreTokensPerBlock];   // 32 KB
     __shared__ __attribute__((aligned(16))) float qc_lds[kHeadBlock][kLabelDims];
     __shared__ uint32_t lo_lds[kHeadBlock];
-    __shared__ __attribute__((aligned(16))) uint32_t img_all[kScoreWaves][kRecWords];
     const int b = blockIdx.z;
     const int g = blockIdx.y / head_blocks, hb = blockIdx.y - g * head_blocks;
     const int n = seq_lens[b];
@@ -80,114 +83,133 @@ __global__ __launch_bounds__(kScoreWaves * 64, 2) void label_score_kernel(
     const int h0 = g * group + hb * kHeadBlock;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int n_wg = min(kScoreTokensPerBlock, n - tok0);     // the workgroup's tokens
-    {
-        const int i = threadIdx.x;
-        const int pages_seq = (n + kPage - 1) / kPage, p_base = tok0 / kPage;
-        if (i < kScoreTokensPerBlock / kPage && p_base + i < pages_seq)
-            pt_lds[i] = page_table[(int64_t)b * max_pages + p_base + i];
-        if (i < heads_here * kLabelDims) {
-            const int h = i / kLabelDims, c = i - h * kLabelDims;
-            qc_lds[h][c] = __uint_as_float(
-                (uint32_t)q[((int64_t)b * num_q_heads + h0 + h) * kHeadDim + channels[g * kLabelDims + c]] << 16);
+    // 1. the lane's 8 label rows in flight (page-table entries, then rows), and the
+    //    q values on the head's channels staged in LDS meanwhile (an LDS-only barrier
+    //    keeps the rows in flight)
+    const bool q_lane = threadIdx.x < heads_here * kLabelDims;   // stages q at one channel of a head
+    const int qh = threadIdx.x / kLabelDims, qcn = threadIdx.x - qh * kLabelDims;
+    int32_t chan = 0;
+    if (q_lane) chan = channels[g * kLabelDims + qcn];
+    const int32_t *pt = page_table + (int64_t)b * max_pages;
+    int32_t phys[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        const int tl = wave * kWaveTokens + 64 * i + lane;
+        phys[i] = pt[(tok0 + min(tl, n_wg - 1)) >> 4];
+    }
+    uint32_t qbits = 0;
+    if (q_lane) qbits = q[((int64_t)b * num_q_heads + h0 + qh) * kHeadDim + chan];
+    u32x4 w[kPer][2];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        const int tl = min(wave * kWaveTokens + 64 * i + lane, n_wg - 1);    // past the row: reload a row of it
+        const int64_t row = ((int64_t)phys[i] * num_kv_heads + g) * kPage + (tl & 15);
+        const u32x4 *lr = (const u32x4 *)(labels + row * kLabelRowElems);
+        w[i][0] = lr[0];
+        w[i][1] = lr[1];
+    }
+    if (q_lane) qc_lds[qh][qcn] = __uint_as_float(qbits << 16);
+    lds_barrier();
+    uint32_t key[kHeadBlock][kPer];
+#pragma unroll
+    for (int h = 0; h < kHeadBlock; ++h) {
+        if (h < heads_here) {                                 // uniform
+            float qc[kLabelDims];
+#pragma unroll
+            for (int c = 0; c < kLabelDims; ++c) qc[c] = qc_lds[h][c];
+#pragma unroll
+            for (int i = 0; i < kPer; ++i) {
+                const int tl = wave * kWaveTokens + 64 * i + lane;
+                key[h][i] = tl < n_wg ? score_key(label_score(qc, w[i][0], w[i][1])) : 0u;
+                if constexpr (!kAllKeys) codes[h][tl] = (uint16_t)(key[h][i] >> 16);
+            }
         }
     }
-    __syncthreads();
-    // 1. s~ of every token for every head: thread t takes tokens t + 256 u
-    u32x4 w[kLblPerThread][2];
-#pragma unroll
-    for (int u = 0; u < kLblPerThread; ++u) {
-        const int tl = threadIdx.x + kScoreWaves * 64 * u;
-        w[u][0] = w[u][1] = u32x4{0u, 0u, 0u, 0u};
-        if (tl < n_wg) {
-            const int64_t row = ((int64_t)pt_lds[tl >> 4] * num_kv_heads + g) * kPage + (tl & 15);
-            const u32x4 *lr = (const u32x4 *)(labels + row * kLabelRowElems);
-            w[u][0] = lr[0];
-            w[u][1] = lr[1];
-        }
-    }
-    for (int h = 0; h < heads_here; ++h) {
-        float qc[kLabelDims];
-#pragma unroll
-        for (int i = 0; i < kLabelDims; ++i) qc[i] = qc_lds[h][i];
-#pragma unroll
-        for (int u = 0; u < kLblPerThread; ++u) {
-            const int tl = threadIdx.x + kScoreWaves * 64 * u;
-            keys_lds[h][tl] = tl < n_wg ? score_key(label_score(qc, w[u][0], w[u][1])) : 0u;
-        }
-    }
-    __syncthreads();
     if constexpr (kAllKeys) {                                 // every key to the head's key row
-        for (int h = 0; h < heads_here; ++h) {
-            uint32_t *krow = keys32 + ((int64_t)b * num_q_heads + h0 + h) * key_stride + tok0;
-            for (int tl = threadIdx.x; tl < n_wg; tl += kScoreWaves * 64) krow[tl] = keys_lds[h][tl];
+#pragma unroll
+        for (int h = 0; h < kHeadBlock; ++h) {
+            if (h < heads_here) {
+                uint32_t *krow = keys32 + ((int64_t)b * num_q_heads + h0 + h) * key_stride + tok0;
+#pragma unroll
+                for (int i = 0; i < kPer; ++i) {
+                    const int tl = wave * kWaveTokens + 64 * i + lane;
+                    if (tl < n_wg) krow[tl] = key[h][i];
+                }
+            }
         }
         return;
-    }
-    // 2. per head (one wave each): the r-th largest code of the workgroup's own keys
-    for (int hh = wave; hh < heads_here; hh += kScoreWaves) {
-        uint32_t b_lo = 0xFFFFFFFFu;                          // k' = 0 or N: no candidates needed
-        if (kk > 0 && kk < n) {
-            const float mu = (float)n_wg * (float)kk / (float)n;
-            const uint32_t r = (uint32_t)ceilf(mu + 6.f * sqrtf(mu) + 8.f);
-            b_lo = 0u;                                        // a small workgroup keeps everything
-            if (r < (uint32_t)n_wg) {
-                uint32_t lo_c = 0, hi_c = 0x10000;            // count(code >= lo_c) >= r > count(code >= hi_c)
-                while (hi_c - lo_c > 1) {
-                    const uint32_t mid = (lo_c + hi_c) >> 1;
-                    uint32_t m = 0;
-                    for (int e = lane; e < kScoreTokensPerBlock; e += 64) m += (keys_lds[hh][e] >> 16) >= mid ? 1u : 0u;
-                    if (wave_total(m) >= r) lo_c = mid; else hi_c = mid;
+    } else {
+        __syncthreads();
+        // 2. per head (one wave each): the r-th largest code of the workgroup's own keys
+        for (int hh = wave; hh < heads_here; hh += kScoreWaves) {
+            uint32_t b_lo = 0xFFFFFFFFu;                      // k' = 0 or N: no candidates needed
+            if (kk > 0 && kk < n) {
+                const float mu = (float)n_wg * (float)kk / (float)n;
+                const uint32_t r = (uint32_t)ceilf(mu + 6.f * sqrtf(mu) + 8.f);
+                b_lo = 0u;                                    // a small workgroup keeps everything
+                if (r < (uint32_t)n_wg) {
+                    constexpr int per_lane = kScoreTokensPerBlock / 64;   // 32 codes, 16-byte reads
+                    uint32_t c[per_lane];
+#pragma unroll
+                    for (int v = 0; v < per_lane / 8; ++v) {
+                        const u32x4 w4 = *(const u32x4 *)&codes[hh][lane * per_lane + 8 * v];
+                        c[8 * v + 0] = w4.x & 0xFFFFu; c[8 * v + 1] = w4.x >> 16;
+                        c[8 * v + 2] = w4.y & 0xFFFFu; c[8 * v + 3] = w4.y >> 16;
+                        c[8 * v + 4] = w4.z & 0xFFFFu; c[8 * v + 5] = w4.z >> 16;
+                        c[8 * v + 6] = w4.w & 0xFFFFu; c[8 * v + 7] = w4.w >> 16;
+                    }
+                    uint32_t lo_c = 0, hi_c = 0x10000;        // count(code >= lo_c) >= r > count(code >= hi_c)
+                    while (hi_c - lo_c > 1) {
+                        const uint32_t mid = (lo_c + hi_c) >> 1;
+                        uint32_t m = 0;
+#pragma unroll
+                        for (int e = 0; e < per_lane; ++e) m += c[e] >= mid ? 1u : 0u;
+                        if (wave_total(m) >= r) lo_c = mid; else hi_c = mid;
+                    }
+                    b_lo = lo_c << 16;
                 }
-                b_lo = lo_c << 16;
+            }
+            if (lane == 0) lo_lds[hh] = b_lo;
+        }
+        __syncthreads();
+        // 3. the records: wave w writes slot w of each head straight from its registers;
+        //    candidates (keys >= the bound) are placed in token order by ballot; a store
+        //    past the record's 192 entries (an overflowed slot) aims past the row and is
+        //    dropped by the buffer range check, and the header marks the overflow
+        const int s_tok0 = tok0 + wave * kWaveTokens;
+        if (s_tok0 >= n) return;                              // wave-uniform
+        const int slot = s_tok0 / kWaveTokens;
+        const uint32_t row_bytes = (uint32_t)slots * kRecWords * 4u;
+        const uint32_t rec0 = (uint32_t)slot * kRecWords * 4u;
+#pragma unroll
+        for (int h = 0; h < kHeadBlock; ++h) {
+            if (h < heads_here) {
+                const uint32_t lo = lo_lds[h];
+                const int64_t row_h = (int64_t)b * num_q_heads + h0 + h;
+                const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+                    cand_rec + row_h * slots * kRecWords, 0, (int)row_bytes, kBufferDword3);
+                uint32_t cnt = 0, kmax = 0;
+#pragma unroll
+                for (int i = 0; i < kPer; ++i) {
+                    const int tl = wave * kWaveTokens + 64 * i + lane;
+                    const bool take = tl < n_wg && key[h][i] >= lo;
+                    const uint64_t m = __ballot(take);
+                    const uint32_t pos = cnt + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                                         __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+                    const bool put = take && pos < (uint32_t)kCandCap;
+                    __builtin_amdgcn_raw_buffer_store_b32(key[h][i], rsrc, put ? rec0 + 4u * pos : kDropOffset, 0, 0);
+                    __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(64 * i + lane), rsrc,
+                                                          put ? rec0 + (kCandCap + 4) * 4u + 2u * pos : kDropOffset,
+                                                          0, 0);
+                    kmax = max(kmax, take ? key[h][i] : 0u);
+                    cnt += (uint32_t)__popcll(m);
+                }
+#pragma unroll
+                for (int o = 32; o > 0; o >>= 1) kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o, 64));
+                const u32x4 hdr = u32x4{cnt > (uint32_t)kCandCap ? kCandOverflow : cnt, lo, kmax, 0u};
+                __builtin_amdgcn_raw_buffer_store_b128(hdr, rsrc, lane == 0 ? rec0 + kCandCap * 4u : kDropOffset, 0, 0);
             }
         }
-        if (lane == 0) lo_lds[hh] = b_lo;
-    }
-    __syncthreads();
-    // 3. the records: wave w takes the workgroup's slot w, head by head; candidates
-    //    (keys >= the bound) in token order by ballot, assembled in LDS, written out in
-    //    whole 128-byte lines through a buffer resource (dropped lanes aim past the row)
-    const int s_tok0 = tok0 + wave * kWaveTokens;
-    if (s_tok0 >= n) return;                                  // wave-uniform
-    const int slot = s_tok0 / kWaveTokens;
-    uint32_t *img = img_all[wave];
-    uint16_t *img_pos = (uint16_t *)(img + kCandCap + 4);
-    const uint32_t row_bytes = (uint32_t)slots * kRecWords * 4u;
-    const uint32_t at = (uint32_t)slot * kRecWords * 4u + 16u * lane;
-    for (int h = 0; h < heads_here; ++h) {
-        const uint32_t lo = lo_lds[h];
-        uint32_t cnt = 0, kmax = 0;
-#pragma unroll
-        for (int i = 0; i < kWaveTokens / 64; ++i) {
-            const int tl = wave * kWaveTokens + 64 * i + lane;
-            const uint32_t key = keys_lds[h][tl];
-            const bool take = tok0 + tl < n && key >= lo;
-            const uint64_t m = __ballot(take);
-            const uint32_t pos = cnt + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
-                                                                 __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-            if (take && pos < (uint32_t)kCandCap) {
-                img[pos] = key;
-                img_pos[pos] = (uint16_t)(64 * i + lane);
-            }
-            kmax = max(kmax, take ? key : 0u);
-            cnt += (uint32_t)__popcll(m);
-        }
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o, 64));
-        const bool ovf = cnt > (uint32_t)kCandCap;
-        if (lane == 0) *(u32x4 *)(img + kCandCap) = u32x4{ovf ? kCandOverflow : cnt, lo, kmax, 0u};
-        wave_lds_sync();
-        const int64_t row_h = (int64_t)b * num_q_heads + h0 + h;
-        const __amdgpu_buffer_rsrc_t rsrc =
-            __builtin_amdgcn_make_buffer_rsrc(cand_rec + row_h * slots * kRecWords, 0, (int)row_bytes, kBufferDword3);
-        const uint32_t tot = ovf ? 0u : cnt;
-        const int key_chunks = (int)((tot + 31u) / 32u) * 8;
-        const int tail_chunks = (int)((4u + (tot + 1u) / 2u + 31u) / 32u) * 8;
-        const u32x4 kv = ((const u32x4 *)img)[min(lane, kCandCap / 4 - 1)];
-        const u32x4 tv = ((const u32x4 *)(img + kCandCap))[min(lane, kRecTailWords / 4 - 1)];
-        __builtin_amdgcn_raw_buffer_store_b128(kv, rsrc, lane < key_chunks ? at : kDropOffset, 0, 0);
-        __builtin_amdgcn_raw_buffer_store_b128(tv, rsrc, lane < tail_chunks ? at + kCandCap * 4 : kDropOffset, 0, 0);
-        wave_lds_sync();                                      // the image is free for the next head
     }
 }
 
