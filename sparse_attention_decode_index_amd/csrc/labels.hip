@@ -15,7 +15,7 @@
 //     sequence's current page after an append).
 //  2. label_score_kernel   per (b, kv head, 2048 tokens): s~ of the workgroup's
 //     tokens for its q heads (16-byte label loads, all in flight; keys stay in the
-//     registers of the lane that scored them, their top 16 bits go to LDS), then per
+//     registers of the lane that scored them, their top 15 bits go to LDS), then per
 //     head the workgroup's bound (bisection on those codes for the r-th largest of its
 //     own scores, r = mu + 6 sqrt(mu) + 8, mu = n_w k / N) and, per 512-token slot,
 //     the candidate record (ballot placement in token order) that the exact
@@ -121,7 +121,7 @@ __global__ __launch_bounds__(kScoreWaves * 64, 3) void label_score_kernel(
             for (int i = 0; i < kPer; ++i) {
                 const int tl = wave * kWaveTokens + 64 * i + lane;
                 key[h][i] = tl < n_wg ? score_key(label_score(qc, w[i][0], w[i][1])) : 0u;
-                if constexpr (!kAllKeys) codes[h][tl] = (uint16_t)(key[h][i] >> 16);
+                if constexpr (!kAllKeys) codes[h][tl] = (uint16_t)(key[h][i] >> 17);
             }
         }
     }
@@ -148,25 +148,29 @@ __global__ __launch_bounds__(kScoreWaves * 64, 3) void label_score_kernel(
                 const uint32_t r = (uint32_t)ceilf(mu + 6.f * sqrtf(mu) + 8.f);
                 b_lo = 0u;                                    // a small workgroup keeps everything
                 if (r < (uint32_t)n_wg) {
-                    constexpr int per_lane = kScoreTokensPerBlock / 64;   // 32 codes, 16-byte reads
-                    uint32_t c[per_lane];
+                    // the lane's 32 codes, two per word (16-byte reads).  A code is the
+                    // top 15 bits of a key, so code >= mid is bit 15 of (code | 0x8000) - mid:
+                    // two compares per subtract, counted by bit count
+                    constexpr int words = kScoreTokensPerBlock / 64 / 2;
+                    uint32_t cw[words];
 #pragma unroll
-                    for (int v = 0; v < per_lane / 8; ++v) {
-                        const u32x4 w4 = *(const u32x4 *)&codes[hh][lane * per_lane + 8 * v];
-                        c[8 * v + 0] = w4.x & 0xFFFFu; c[8 * v + 1] = w4.x >> 16;
-                        c[8 * v + 2] = w4.y & 0xFFFFu; c[8 * v + 3] = w4.y >> 16;
-                        c[8 * v + 4] = w4.z & 0xFFFFu; c[8 * v + 5] = w4.z >> 16;
-                        c[8 * v + 6] = w4.w & 0xFFFFu; c[8 * v + 7] = w4.w >> 16;
+                    for (int v = 0; v < words / 4; ++v) {
+                        const u32x4 w4 = *(const u32x4 *)&codes[hh][lane * 2 * words + 8 * v];
+                        cw[4 * v + 0] = w4.x | 0x80008000u; cw[4 * v + 1] = w4.y | 0x80008000u;
+                        cw[4 * v + 2] = w4.z | 0x80008000u; cw[4 * v + 3] = w4.w | 0x80008000u;
                     }
-                    uint32_t lo_c = 0, hi_c = 0x10000;        // count(code >= lo_c) >= r > count(code >= hi_c)
+                    uint32_t lo_c = 0, hi_c = 0x8000;         // count(code >= lo_c) >= r > count(code >= hi_c)
                     while (hi_c - lo_c > 1) {
-                        const uint32_t mid = (lo_c + hi_c) >> 1;
-                        uint32_t m = 0;
+                        const uint32_t mid = (lo_c + hi_c) >> 1, mid2 = mid | (mid << 16);
+                        uint32_t m0 = 0, m1 = 0;
 #pragma unroll
-                        for (int e = 0; e < per_lane; ++e) m += c[e] >= mid ? 1u : 0u;
-                        if (wave_total(m) >= r) lo_c = mid; else hi_c = mid;
+                        for (int e = 0; e < words; e += 2) {
+                            m0 += __popc((cw[e] - mid2) & 0x80008000u);
+                            m1 += __popc((cw[e + 1] - mid2) & 0x80008000u);
+                        }
+                        if (wave_total(m0 + m1) >= r) lo_c = mid; else hi_c = mid;
                     }
-                    b_lo = lo_c << 16;
+                    b_lo = lo_c << 17;
                 }
             }
             if (lane == 0) lo_lds[hh] = b_lo;
