@@ -35,6 +35,14 @@ sparse-attention survey blog):
   of highest bound.  Pinned by the box property of min/max, the bound dominating
   every token score of its page (tight for constant pages, closed forms for
   one-signed queries), brute force over page subsets, and m >= pages giving dense.
+* ``sample_residual`` / ``attend_sampled``  stochastic index selection (the German
+  summary, sections 2 and 3A, vAttention; its estimator is not on the pages, so the
+  plain Monte Carlo reading): the top-k set plus s' tokens drawn uniformly with
+  replacement from the rest (M tokens), each drawn token weighted M / s' in the
+  softmax sums.  Pinned by draws that enumerate the residual (once: weight 1, the
+  rest exactly; twice: weight 1/2) giving dense attention, by the residual list
+  against a set difference, and by residuals of identical rows, where any draw gives
+  the dense output exactly.
 """
 from __future__ import annotations
 
@@ -75,6 +83,8 @@ def _declare(lib):
     lib.oracle_quest_summaries.argtypes = [p, p, p, i32, i32, i32, p]
     lib.oracle_quest_bounds.argtypes = [p, p, i32, i32, i32, p, i32, p]
     lib.oracle_quest_select.argtypes = [p, p, p, i32, i32, i32, i32, p, p, p]
+    lib.oracle_sample_residual.argtypes = [p, p, i32, p, i32, i32, p, p, i32, p, p]
+    lib.oracle_attend_sampled.argtypes = [p, p, p, p, i32, i32, i32, p, i32, p, i32, p, i32, p, f64, p]
     return lib
 
 
@@ -230,4 +240,38 @@ def label_scores(cache: Cache, q, channels, lib=None) -> np.ndarray:
     out = np.full((cache.batch, hq, n_max), np.nan)
     lib.oracle_label_scores(cache.kp, cache.ptp, cache.slp, cache.batch, cache.num_kv_heads, cache.max_pages,
                             qp, hq, chp, ch.shape[1], n_max, out.ctypes.data_as(ctypes.c_void_p))
+    return out
+
+
+def sample_residual(idx, k_per_seq, seq_lens, draws, s_per_seq, lib=None):
+    """(sample [B][Hq][s_max] int32, weight [B][Hq] fp64): draw t of row (b, h) is the
+    residual token of rank floor(draws[b,h,t] M / 2^32), M = N_b - |kept set|; weight
+    M / s'_b, s'_b = min(s_b, s_max) (0 and -1 entries when nothing is drawn)."""
+    lib = lib or _load()
+    ix, ixp = _c(idx, np.int32)
+    kk, kkp = _c(k_per_seq, np.int32)
+    sl, slp = _c(seq_lens, np.int32)
+    dr, drp = _c(draws, np.uint32)
+    ss, ssp = _c(s_per_seq, np.int32)
+    B, hq, k_max = ix.shape
+    s_max = dr.shape[2]
+    sample = np.empty((B, hq, s_max), dtype=np.int32)
+    weight = np.empty((B, hq), dtype=np.float64)
+    lib.oracle_sample_residual(ixp, kkp, k_max, slp, B, hq, drp, ssp, s_max, sample.ctypes.data_as(ctypes.c_void_p),
+                               weight.ctypes.data_as(ctypes.c_void_p))
+    return sample, weight
+
+
+def attend_sampled(cache: Cache, q, idx, sample, weight, scale: float = DEFAULT_SCALE, lib=None) -> np.ndarray:
+    """fp64 stochastic estimate [B][Hq][128]: softmax sums over idx (weight 1) and
+    sample (weight[b,h] per entry), -1 entries skipped."""
+    lib = lib or _load()
+    q, qp = _c(q, np.uint16)
+    ix, ixp = _c(idx, np.int32)
+    sm, smp = _c(sample, np.int32)
+    w, wp = _c(weight, np.float64)
+    B, hq, k_max = ix.shape
+    out = np.empty((B, hq, 128), dtype=np.float64)
+    lib.oracle_attend_sampled(cache.kp, cache.vp, cache.ptp, cache.slp, B, cache.num_kv_heads, cache.max_pages,
+                              qp, hq, ixp, k_max, smp, sm.shape[2], wp, scale, out.ctypes.data_as(ctypes.c_void_p))
     return out

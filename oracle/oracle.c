@@ -368,3 +368,99 @@ void oracle_label_scores(const uint16_t *k_cache, const int32_t *page_table, con
         }
     }
 }
+
+/*
+ * Stochastic index selection.  The German summary of the context-sparsity paper
+ * (section 2, sparsity mechanisms, and section 3A) evaluates vAttention's stochastic
+ * selection, which on smaller models recovers the quality that deterministic top-k
+ * loses; the pages do not give its estimator.  The reading taken here is the plain
+ * Monte Carlo one: keep the deterministic set S (the valid entries of a top-k row),
+ * draw s' tokens uniformly and with replacement from the residual
+ * R = {0, ..., N_b - 1} \ S (M = |R| tokens), and let every drawn token stand for
+ * M / s' tokens of R, so that (M / s') sum_t f(j_t) estimates sum_{j in R} f(j)
+ * without bias.  The random numbers are inputs: draw t of row (b, h) is a 32-bit
+ * integer x_t, mapped to the residual rank r_t = floor(x_t M / 2^32) and then to the
+ * r_t-th token of R in ascending order.
+ *
+ * idx [B][Hq][k_max]: the first min(k_b, k_max) entries of a row are read and those
+ * in [0, N_b) form S.  draws uint32 [B][Hq][s_max]; s_per_seq [B]; s'_b =
+ * min(s_b, s_max), 0 when M = 0.  sample_out [B][Hq][s_max]: the drawn tokens, -1
+ * from t = s'_b on.  weight_out [B][Hq]: M / s'_b (0 when nothing is drawn).
+ */
+void oracle_sample_residual(const int32_t *idx, const int32_t *k_per_seq, int32_t k_max, const int32_t *seq_lens,
+                            int32_t batch, int32_t num_q_heads, const uint32_t *draws, const int32_t *s_per_seq,
+                            int32_t s_max, int32_t *sample_out, double *weight_out)
+{
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t bh = 0; bh < (int64_t)batch * num_q_heads; ++bh) {
+        int b = (int)(bh / num_q_heads);
+        int64_t n = seq_lens[b] > 0 ? seq_lens[b] : 0;
+        int64_t kk = k_per_seq[b] < k_max ? k_per_seq[b] : k_max;
+        if (kk < 0) kk = 0;
+        char *kept = (char *)calloc((size_t)(n > 0 ? n : 1), 1);
+        for (int64_t i = 0; i < kk; ++i) {
+            int32_t j = idx[bh * k_max + i];
+            if (j >= 0 && j < n) kept[j] = 1;
+        }
+        int32_t *residual = (int32_t *)malloc((size_t)(n > 0 ? n : 1) * sizeof *residual);
+        int64_t M = 0;
+        for (int64_t j = 0; j < n; ++j)
+            if (!kept[j]) residual[M++] = (int32_t)j;
+        int64_t s = s_per_seq[b] < s_max ? s_per_seq[b] : s_max;
+        if (s < 0 || M == 0) s = 0;
+        for (int64_t t = 0; t < s_max; ++t) {
+            int32_t tok = -1;
+            if (t < s) {
+                uint64_t r = ((uint64_t)draws[bh * s_max + t] * (uint64_t)M) >> 32;
+                tok = residual[r];
+            }
+            sample_out[bh * s_max + t] = tok;
+        }
+        weight_out[bh] = s > 0 ? (double)M / (double)s : 0.0;
+        free(residual);
+        free(kept);
+    }
+}
+
+/*
+ * The stochastic estimate of the attention output: the kept entries (idx, weight 1)
+ * and the drawn ones (sample, weight w_bh each) enter the softmax sums as
+ *     o = (sum_S e^{l_j} V_j + w sum_t e^{l_{j_t}} V_{j_t}) / (sum_S e^{l_j} + w sum_t e^{l_{j_t}}),
+ * l_j = c s_j as in attend (with the same max subtraction).  Entries < 0 are skipped;
+ * a token drawn twice counts twice.  out [B][Hq][128] fp64.
+ */
+void oracle_attend_sampled(const uint16_t *k_cache, const uint16_t *v_cache, const int32_t *page_table,
+                           const int32_t *seq_lens, int32_t batch, int32_t num_kv_heads, int32_t max_pages,
+                           const uint16_t *q, int32_t num_q_heads, const int32_t *idx, int32_t k_max,
+                           const int32_t *sample, int32_t s_max, const double *weight, double scale, double *out)
+{
+    orc_cache c = {k_cache, v_cache, page_table, seq_lens, batch, num_kv_heads, max_pages};
+    int32_t G = num_q_heads / num_kv_heads;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t bh = 0; bh < (int64_t)batch * num_q_heads; ++bh) {
+        int b = (int)(bh / num_q_heads), g = (int)(bh % num_q_heads) / G;
+        const uint16_t *qrow = q + bh * ORC_D;
+        int64_t total = (int64_t)k_max + s_max;
+        double m = -INFINITY;
+        for (int64_t i = 0; i < total; ++i) {
+            int32_t j = i < k_max ? idx[bh * k_max + i] : sample[bh * s_max + (i - k_max)];
+            if (j < 0) continue;
+            double l = scale * dot_q_k(qrow, row_of(c.k, &c, b, g, j));
+            if (l > m) m = l;
+        }
+        double z = 0.0, acc[ORC_D];
+        for (int d = 0; d < ORC_D; ++d) acc[d] = 0.0;
+        for (int64_t i = 0; i < total; ++i) {
+            int32_t j = i < k_max ? idx[bh * k_max + i] : sample[bh * s_max + (i - k_max)];
+            if (j < 0) continue;
+            double wt = i < k_max ? 1.0 : weight[bh];
+            double p = wt * exp(scale * dot_q_k(qrow, row_of(c.k, &c, b, g, j)) - m);
+            const uint16_t *vrow = row_of(c.v, &c, b, g, j);
+            z += p;
+            for (int d = 0; d < ORC_D; ++d)
+                acc[d] += p * bf16_value(vrow[d]);
+        }
+        for (int d = 0; d < ORC_D; ++d)
+            out[bh * ORC_D + d] = z > 0.0 ? acc[d] / z : 0.0;
+    }
+}

@@ -21,6 +21,11 @@ None of them recomputes a result the way the oracle does:
            selected gives dense attention;
 * labels:  all channels (or keys vanishing off the channel set) give the full
            scores bit for bit; exact rationals on a tiny case.
+* sampling: draws that enumerate the residual ranks give the set difference of the
+           context and the kept set, in order, with weight 1; the ends of the 32-bit
+           range give its first and last token; an empty residual, s = 0 and s > s_max;
+           enumerating the residual once (weight 1) or twice (weight 1/2) gives dense
+           attention; a residual of identical rows gives dense attention for any draws.
 """
 from __future__ import annotations
 
@@ -444,10 +449,116 @@ def pin_label_scores(lib):
                 assert abs(got[b, h, j] - float(want)) <= 1e-12 * (1 + abs(float(want)))
 
 
+# ---------------------------------------------------------------------------- stochastic selection
+
+def _enumerating_draws(M, reps=1):
+    """32-bit draws whose ranks floor(x M / 2^32) are 0, 1, ..., M-1 (each reps times)."""
+    ranks = [r for r in range(M) for _ in range(reps)]
+    return [(r * 2 ** 32 + M - 1) // M for r in ranks]
+
+
+def _kept_rows(rng, lens, hq, k_max, kvec):
+    """Random kept sets in the top-k row format: ascending valid tokens, then -1."""
+    B = len(lens)
+    idx = np.full((B, hq, k_max), -1, np.int32)
+    for b in range(B):
+        kp = min(int(kvec[b]), k_max, int(lens[b]))
+        for h in range(hq):
+            idx[b, h, :kp] = np.sort(rng.choice(int(lens[b]), size=kp, replace=False))
+    return idx
+
+
+def pin_sample_enumeration(lib):
+    rng = np.random.default_rng(36)
+    lens = np.array([30, 7, 12, 50], np.int32)
+    kvec = np.array([5, 7, 0, 9], np.int32)          # row 1 keeps everything: empty residual
+    hq, k_max, s_max = 3, 10, 50
+    idx = _kept_rows(rng, lens, hq, k_max, kvec)
+    draws = np.zeros((4, hq, s_max), np.uint32)
+    svec = np.zeros(4, np.int32)
+    for b in range(4):
+        M = int(lens[b]) - min(int(kvec[b]), int(lens[b]))
+        svec[b] = max(M, 1)
+        for h in range(hq):
+            draws[b, h, :M] = _enumerating_draws(M) if M else []
+    sample, weight = oracle.sample_residual(idx, kvec, lens, draws, svec, lib=lib)
+    for b in range(4):
+        for h in range(hq):
+            kept = set(idx[b, h][idx[b, h] >= 0].tolist())
+            rest = sorted(set(range(int(lens[b]))) - kept)
+            M = len(rest)
+            assert sample[b, h, :M].tolist() == rest, (b, h)
+            assert np.all(sample[b, h, M:] == -1)
+            assert weight[b, h] == (1.0 if M else 0.0)
+    # the ends of the 32-bit range; s > s_max is clipped; s = 0 draws nothing
+    d2 = np.zeros((4, hq, 2), np.uint32)
+    d2[..., 1] = 2 ** 32 - 1
+    sample, weight = oracle.sample_residual(idx, kvec, lens, d2, np.array([5, 5, 0, 2], np.int32), lib=lib)
+    for b, h in itertools.product(range(4), range(hq)):
+        rest = sorted(set(range(int(lens[b]))) - set(idx[b, h][idx[b, h] >= 0].tolist()))
+        if b in (1, 2):
+            assert sample[b, h].tolist() == [-1, -1] and weight[b, h] == 0.0
+        else:
+            assert sample[b, h].tolist() == [rest[0], rest[-1]] and weight[b, h] == len(rest) / 2
+
+
+def pin_sampled_enumeration_is_dense(lib):
+    """Every residual token drawn once (weight 1) or twice (weight 1/2): the estimate is
+    the dense output."""
+    rng = np.random.default_rng(37)
+    case = random_case(rng, batch=3, hq=4, hkv=2, lens=[23, 40, 9], layout="fragmented")
+    c = _cache(case)
+    kvec = np.array([6, 11, 3], np.int32)
+    idx, _ = oracle.topk(oracle.scores(c, case.q, lib=lib), c.sl, kvec, 11, lib=lib)
+    dense = oracle.dense(c, case.q, SCALE, lib=lib)
+    for reps in (1, 2):
+        s_max = 2 * 40
+        draws = np.zeros((3, 4, s_max), np.uint32)
+        svec = np.zeros(3, np.int32)
+        for b in range(3):
+            M = int(case.lens[b]) - int(kvec[b])
+            svec[b] = reps * M
+            draws[b, :, :reps * M] = _enumerating_draws(M, reps)
+        sample, weight = oracle.sample_residual(idx, kvec, c.sl, draws, svec, lib=lib)
+        for b in range(3):
+            assert np.all(weight[b] == 1.0 / reps)
+        est = oracle.attend_sampled(c, case.q, idx, sample, weight, SCALE, lib=lib)
+        assert np.allclose(est, dense, rtol=1e-12, atol=1e-14), reps
+
+
+def pin_sampled_identical_residual(lib):
+    """All tokens outside the kept set share one key row and one value row: whatever
+    is drawn, M / s' copies per draw rebuild the residual's sums exactly."""
+    rng = np.random.default_rng(38)
+    lens = [37, 64]
+    hkv, hq, k_max = 2, 4, 8
+    kvec = np.array([5, 8], np.int32)
+    idx = _kept_rows(rng, np.array(lens, np.int32), hq, k_max, kvec)
+    k = [bf16_round(rng.standard_normal((hkv, n, 128))) for n in lens]
+    v = [bf16_round(rng.standard_normal((hkv, n, 128))) for n in lens]
+    for b, n in enumerate(lens):
+        kept = set(idx[b, 0][idx[b, 0] >= 0].tolist())
+        for h in range(1, hq):
+            idx[b, h] = idx[b, 0]                     # one kept set per sequence
+        krow, vrow = bf16_round(rng.standard_normal((2, hkv, 128)))
+        for j in range(n):
+            if j not in kept:
+                k[b][:, j], v[b][:, j] = krow, vrow
+    case = TinyCase(k, v, bf16_round(rng.standard_normal((2, hq, 128))), layout="shuffled")
+    c = _cache(case)
+    dense = oracle.dense(c, case.q, SCALE, lib=lib)
+    for s in (1, 3, 7):
+        draws = rng.integers(0, 2 ** 32, size=(2, hq, 7), dtype=np.uint64).astype(np.uint32)
+        sample, weight = oracle.sample_residual(idx, kvec, c.sl, draws, np.array([s, s], np.int32), lib=lib)
+        est = oracle.attend_sampled(c, case.q, idx, sample, weight, SCALE, lib=lib)
+        assert np.allclose(est, dense, rtol=1e-12, atol=1e-14), s
+
+
 ALL_PINS = [
     pin_topk_bruteforce, pin_topk_rank_count, pin_scores_exact, pin_scores_integer,
     pin_shift_invariance, pin_attend_decimal, pin_uniform_values, pin_uniform_keys, pin_one_hot,
     pin_k1_argmax_row, pin_dense_is_attend_all, pin_layout_invariance,
     pin_quest_box, pin_quest_bound, pin_quest_select_bruteforce, pin_quest_all_pages_is_dense,
     pin_label_scores,
+    pin_sample_enumeration, pin_sampled_enumeration_is_dense, pin_sampled_identical_residual,
 ]

@@ -60,6 +60,17 @@ MUTANTS = {
                                       "for (int i = 1; i < r; ++i)\n                s += bf16_value(qrow[ch[i]])"),
     "k not clamped to k_max": ("if (kk > k_max) kk = k_max;\n        if (kk < 0) kk = 0;",
                                "if (kk > k_max) kk = k_max - 1;\n        if (kk < 0) kk = 0;"),
+    "sample rank off by one": ("tok = residual[r];", "tok = residual[(r + 1) % M];"),
+    "sample draws from the whole context": ("if (!kept[j]) residual[M++] = (int32_t)j;",
+                                            "residual[M++] = (int32_t)j;"),
+    "sample weight dropped": ("weight_out[bh] = s > 0 ? (double)M / (double)s : 0.0;",
+                              "weight_out[bh] = s > 0 ? 1.0 : 0.0;"),
+    "sample weight over s + 1 draws": ("weight_out[bh] = s > 0 ? (double)M / (double)s : 0.0;",
+                                       "weight_out[bh] = s > 0 ? (double)M / (double)(s + 1) : 0.0;"),
+    "sample weight on the kept entries": ("double wt = i < k_max ? 1.0 : weight[bh];",
+                                          "double wt = i < k_max ? weight[bh] : 1.0;"),
+    "sample weight left out of the denominator": ("            z += p;\n            for (int d = 0; d < ORC_D; ++d)\n                acc[d] += p * bf16_value(vrow[d]);",
+                                                  "            z += p / wt;\n            for (int d = 0; d < ORC_D; ++d)\n                acc[d] += p * bf16_value(vrow[d]);"),
 }
 
 
