@@ -51,6 +51,8 @@ def parse_args():
     ap.add_argument("--labels", action="store_true",
                     help="also time the lightweight indexer on 16-channel label rows (current-page label "
                          "update, label index, attend), with its recall of the exact top-k")
+    ap.add_argument("--sampled", action="store_true",
+                    help="also time the stochastic step (top-k/2 plus k/2 uniform draws from the rest)")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="after timing, copy a buffer of this many MiB 3 times (a plain device copy of known "
                          "size, the reference for scaling memory-traffic counters)")
@@ -87,7 +89,7 @@ def read_traffic():
 def source_sha():
     import hashlib
     h = hashlib.sha256()
-    for f in ("index_topk.hip", "sdi_device.hpp"):
+    for f in ("index_topk.hip", "sdi_device.hpp", "sdi_radix.hpp", "sdi_index.hpp"):
         h.update(open(os.path.join(ROOT, "sparse_attention_decode_index_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
 
@@ -248,6 +250,78 @@ def labels_leg(sdi, wl, kv_full, step_args, timed_graph, per, reps, k_max, idx, 
     res = {"channels": 16, "label_update_us": t_upd * 1e6, "index_us": t_idx * 1e6, "attend_us": t_att * 1e6,
            "step_us": t_step * 1e6, "recall_of_exact_topk": float(np.mean(rec)),
            "index_bytes_per_launch": int((wl.num_kv_heads * n * 32).sum())}
+    if dense_s is not None:
+        res["speedup_vs_dense"] = dense_s / t_step
+    return res
+
+
+def sampled_leg(sdi, wl, kv_full, step_args, timed_graph, per, reps, n_q, k_max, idx, out, ws_index, dense_s):
+    """Stochastic step at the same total budget k: the exact top-ceil(k/2), floor(k/2)
+    uniform draws from the remaining tokens (each weighted by the remaining count over
+    the draws), then the two-list attend.  The draws are inputs, made once on the host
+    and resident like the queries.  Quality on this data: the mean relative L2 error of
+    the output against dense decode, for this estimate and for exact top-k at budget k."""
+    import torch
+    dev = idx.device
+    B, hq = wl.batch, wl.num_q_heads
+    kd_max, s_max = (k_max + 1) // 2, max(1, k_max // 2)
+    split = {}
+    for j in range(n_q):
+        kps = step_args(j)[2]
+        if id(kps) not in split:
+            split[id(kps)] = ((kps + 1) // 2, kps // 2)
+    rng = np.random.default_rng(wl.seed + 7)
+    draws = torch.from_numpy(rng.integers(0, 2 ** 32, size=(B, hq, s_max), dtype=np.uint64)
+                             .astype(np.uint32).view(np.int32)).to(dev)
+    kidx = torch.empty((B, hq, kd_max), dtype=torch.int32, device=dev)
+    sample = torch.empty((B, hq, s_max), dtype=torch.int32, device=dev)
+    weight = torch.empty((B, hq), dtype=torch.float32, device=dev)
+    ws_s = torch.empty(max(1, sdi.attend_sampled_workspace_bytes(kv_full, hq, kd_max, s_max)), dtype=torch.uint8,
+                       device=dev)
+
+    def index(s):
+        kv, q, kps = step_args(s)
+        sdi.index_topk(kv, q, split[id(kps)][0], kd_max, idx_out=kidx, workspace=ws_index,
+                       stream=torch.cuda.current_stream())
+
+    def draw(s):
+        kv, q, kps = step_args(s)
+        kd, sv = split[id(kps)]
+        sdi.sample_residual(kv, kidx, kd, draws, sv, sample_out=sample, weight_out=weight,
+                            stream=torch.cuda.current_stream())
+
+    def attend(s):
+        kv, q, kps = step_args(s)
+        kd, sv = split[id(kps)]
+        sdi.attend_sampled(kv, q, kidx, kd, sample, weight, sv, out=out, workspace=ws_s,
+                           stream=torch.cuda.current_stream())
+
+    def step(s):
+        index(s)
+        draw(s)
+        attend(s)
+
+    for s in range(3):
+        step(s)
+    torch.cuda.synchronize()
+    t_idx, _ = timed_graph(index, max(1, reps), per)
+    t_smp, _ = timed_graph(draw, max(1, reps), per)
+    t_att, _ = timed_graph(attend, max(1, reps), per)
+    t_step, _ = timed_graph(step, max(1, reps), per)
+    kv, q, kps = step_args(0)
+    step(0)
+    est = out.clone()
+    sdi.index_topk(kv, q, kps, k_max, idx_out=idx)
+    ex = sdi.attend(kv, q, idx, kps)
+    dn = sdi.dense(kv, q)
+    torch.cuda.synchronize()
+
+    def rel(o):
+        return float(((o - dn).norm(dim=-1) / dn.norm(dim=-1).clamp_min(1e-30)).mean())
+
+    res = {"kept": "ceil(k/2)", "draws": "floor(k/2)", "index_us": t_idx * 1e6, "sample_us": t_smp * 1e6,
+           "attend_us": t_att * 1e6, "step_us": t_step * 1e6,
+           "rel_err_vs_dense": {"stochastic": rel(est), "exact_topk_k": rel(ex)}}
     if dense_s is not None:
         res["speedup_vs_dense"] = dense_s / t_step
     return res
@@ -423,6 +497,11 @@ def main():
         labels = labels_leg(sdi, wl, kv_full, step_args, timed_graph, per, reps, k_max, idx, out, ws_index,
                             ws_attend, dense_s)
 
+    sampled = None
+    if args.sampled and args.mode == "graph":
+        sampled = sampled_leg(sdi, wl, kv_full, step_args, timed_graph, per, reps, n_q, k_max, idx, out, ws_index,
+                              dense_s)
+
     cold = {}
     if args.cold:
         flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -479,6 +558,8 @@ def main():
         result["quest"] = quest
     if labels is not None:
         result["labels"] = labels
+    if sampled is not None:
+        result["sampled"] = sampled
     result.update(cold)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)      # the host copy is still at step 0

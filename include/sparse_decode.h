@@ -55,7 +55,7 @@ enum {
     SDI_OK = 0,
     SDI_ERR_NULL = -1,       /* a required pointer is NULL */
     SDI_ERR_SHAPE = -2,      /* head_dim != 128, page_size != 16, heads not a multiple, sizes < 1 ... */
-    SDI_ERR_K = -3,          /* k_max < 1 (pages_max < 1 for the page selection) */
+    SDI_ERR_K = -3,          /* k_max < 1 (pages_max < 1 for the page selection, s_max < 1 for draws) */
     SDI_ERR_WORKSPACE = -4,  /* workspace smaller than the *_workspace() size */
     SDI_ERR_HIP = -5         /* a kernel launch failed */
 };
@@ -211,6 +211,48 @@ SDI_API int sparse_decode_quest_select(const sdi_kv *kv, const void *q, int32_t 
                                        void *ws, size_t ws_bytes, void *stream);
 
 SDI_API size_t sparse_decode_quest_select_workspace(const sdi_kv *kv, int32_t num_q_heads, int32_t pages_max);
+
+/*
+ * Stochastic index selection (the German summary of the context-sparsity paper,
+ * sections 2 and 3A: vAttention's stochastic selection recovers on smaller models the
+ * quality deterministic top-k loses).  The pages do not give the estimator; this is
+ * the plain Monte Carlo reading.  A row keeps its top-k set S; s' tokens are drawn
+ * uniformly, with replacement, from the residual R = {0, ..., N_b - 1} \ S (M tokens),
+ * and each drawn token stands for w = M / s' tokens of R in the softmax sums:
+ *     o = (sum_S e^{l_j} V_j + w sum_t e^{l_{j_t}} V_{j_t}) / (sum_S e^{l_j} + w sum_t e^{l_{j_t}}).
+ *
+ * sparse_decode_sample_residual maps caller-supplied random numbers to tokens:
+ *   idx, k_per_seq, k_max  a top-k list as sparse_decode_index_topk writes it: the
+ *             first min(k_b, k_max) entries of a row hold the kept tokens ascending,
+ *             then -1 (other row contents are not validated: the drawn tokens then
+ *             stay in [0, N_b) but do not follow the rule below).
+ *   draws     uint32 [batch][num_q_heads][s_max] device, uniform 32-bit random numbers.
+ *   s_per_seq int32 [batch] device: draws per row s_b; s'_b = min(s_b, s_max), and
+ *             0 when the residual is empty.
+ *   sample_out  int32 [batch][num_q_heads][s_max]: entry t < s'_b is the residual
+ *             token of ascending rank floor(draws[t] * M / 2^32); -1 from s'_b on.
+ *   weight_out  fp32 [batch][num_q_heads]: M / s'_b (0 when nothing is drawn).
+ * No workspace.  k_max < 1 or s_max < 1 returns SDI_ERR_K.
+ *
+ * sparse_decode_attend_sampled evaluates the estimate above: of row (b, h) it reads
+ * the first min(k_b, k_max) entries of idx (weight 1; k_per_seq NULL: all k_max) and
+ * the first min(s_b, s_max) entries of sample (weight sample_weight[b][h] each;
+ * s_per_seq NULL: all s_max), both as the calls above write them; entries outside
+ * [0, N_b) are skipped and a token drawn twice counts twice.  q, softmax_scale, out
+ * as for sparse_decode_attend; ws of sparse_decode_attend_sampled_workspace() bytes.
+ */
+SDI_API int sparse_decode_sample_residual(const sdi_kv *kv, int32_t num_q_heads, const int32_t *idx,
+                                          const int32_t *k_per_seq, int32_t k_max, const uint32_t *draws,
+                                          const int32_t *s_per_seq, int32_t s_max, int32_t *sample_out,
+                                          float *weight_out, void *stream);
+
+SDI_API int sparse_decode_attend_sampled(const sdi_kv *kv, const void *q, int32_t num_q_heads, const int32_t *idx,
+                                         const int32_t *k_per_seq, int32_t k_max, const int32_t *sample,
+                                         const float *sample_weight, const int32_t *s_per_seq, int32_t s_max,
+                                         float softmax_scale, float *out, void *ws, size_t ws_bytes, void *stream);
+
+SDI_API size_t sparse_decode_attend_sampled_workspace(const sdi_kv *kv, int32_t num_q_heads, int32_t k_max,
+                                                      int32_t s_max);
 
 /* Static description of a return code (never NULL). */
 SDI_API const char *sparse_decode_strerror(int code);

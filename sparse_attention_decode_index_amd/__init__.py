@@ -30,6 +30,7 @@ EXPORTS = (
     "sparse_decode_quest_summary_bytes", "sparse_decode_quest_summarize",
     "sparse_decode_quest_select", "sparse_decode_quest_select_workspace",
     "sparse_decode_label_bytes", "sparse_decode_label_build", "sparse_decode_label_index_topk",
+    "sparse_decode_sample_residual", "sparse_decode_attend_sampled", "sparse_decode_attend_sampled_workspace",
 )
 
 
@@ -89,6 +90,12 @@ def load_library(path: str = LIB_PATH):
     lib.sparse_decode_quest_select.restype = ctypes.c_int
     lib.sparse_decode_quest_select_workspace.argtypes = [kvp, i32, i32]
     lib.sparse_decode_quest_select_workspace.restype = sz
+    lib.sparse_decode_sample_residual.argtypes = [kvp, i32, p, p, i32, p, p, i32, p, p, p]
+    lib.sparse_decode_sample_residual.restype = ctypes.c_int
+    lib.sparse_decode_attend_sampled.argtypes = [kvp, p, i32, p, p, i32, p, p, p, i32, f32, p, p, sz, p]
+    lib.sparse_decode_attend_sampled.restype = ctypes.c_int
+    lib.sparse_decode_attend_sampled_workspace.argtypes = [kvp, i32, i32, i32]
+    lib.sparse_decode_attend_sampled_workspace.restype = sz
     lib.sparse_decode_strerror.argtypes = [ctypes.c_int]
     lib.sparse_decode_strerror.restype = ctypes.c_char_p
     if path == LIB_PATH:
@@ -161,6 +168,11 @@ def index_topk_workspace_bytes(kv: PagedKV, num_q_heads: int, k_max: int) -> int
 def attend_workspace_bytes(kv: PagedKV, num_q_heads: int, k_max: int) -> int:
     s = kv.struct()
     return int(load_library().sparse_decode_attend_workspace(ctypes.byref(s), num_q_heads, k_max))
+
+
+def attend_sampled_workspace_bytes(kv: PagedKV, num_q_heads: int, k_max: int, s_max: int) -> int:
+    s = kv.struct()
+    return int(load_library().sparse_decode_attend_sampled_workspace(ctypes.byref(s), num_q_heads, k_max, s_max))
 
 
 def dense_workspace_bytes(kv: PagedKV, num_q_heads: int) -> int:
@@ -318,3 +330,59 @@ def label_index_topk(kv: PagedKV, q, labels, channels, k_per_seq, k_max: int, id
     if rc != SDI_OK:
         raise SparseDecodeError(rc, "sparse_decode_label_index_topk")
     return idx_out
+
+
+def sample_residual(kv: PagedKV, idx, k_per_seq, draws, s_per_seq, sample_out=None, weight_out=None, stream=None):
+    """Uniform draws from the tokens a top-k row left out: (sample int32 [B][Hq][s_max],
+    weight fp32 [B][Hq]).  draws: 32-bit random numbers [B][Hq][s_max] (uint32, or
+    their bits in int32)."""
+    import torch
+    _check(idx, "idx", torch.int32, 3)
+    _check(k_per_seq, "k_per_seq", torch.int32, 1)
+    _check(s_per_seq, "s_per_seq", torch.int32, 1)
+    if draws.dtype not in (torch.int32, torch.uint32) or draws.dim() != 3 or not draws.is_contiguous() \
+            or not draws.is_cuda:
+        raise ValueError("draws must be a contiguous 3-d int32 or uint32 device tensor")
+    B, hq, k_max = idx.shape
+    s_max = int(draws.shape[2])
+    if sample_out is None:
+        sample_out = torch.empty((B, hq, s_max), dtype=torch.int32, device=idx.device)
+    if weight_out is None:
+        weight_out = torch.empty((B, hq), dtype=torch.float32, device=idx.device)
+    s = kv.struct()
+    rc = load_library().sparse_decode_sample_residual(ctypes.byref(s), hq, _ptr(idx), _ptr(k_per_seq), k_max,
+                                                      _ptr(draws), _ptr(s_per_seq), s_max, _ptr(sample_out),
+                                                      _ptr(weight_out), _stream(stream))
+    if rc != SDI_OK:
+        raise SparseDecodeError(rc, "sparse_decode_sample_residual")
+    return sample_out, weight_out
+
+
+def attend_sampled(kv: PagedKV, q, idx, k_per_seq, sample, sample_weight, s_per_seq=None,
+                   softmax_scale: float = DEFAULT_SCALE, out=None, workspace=None, stream=None):
+    """The stochastic estimate: softmax sums over idx (weight 1) and sample (weight
+    sample_weight[b, h] per entry): fp32 [B][Hq][128]."""
+    import torch
+    _check(q, "q", torch.bfloat16, 3)
+    _check(idx, "idx", torch.int32, 3)
+    if k_per_seq is not None:
+        _check(k_per_seq, "k_per_seq", torch.int32, 1)
+    if s_per_seq is not None:
+        _check(s_per_seq, "s_per_seq", torch.int32, 1)
+    _check(sample, "sample", torch.int32, 3)
+    _check(sample_weight, "sample_weight", torch.float32, 2)
+    B, hq, _ = q.shape
+    k_max, s_max = int(idx.shape[2]), int(sample.shape[2])
+    if out is None:
+        out = torch.empty((B, hq, HEAD_DIM), dtype=torch.float32, device=q.device)
+    s = kv.struct()
+    lib = load_library()
+    ws = _workspace(lib.sparse_decode_attend_sampled_workspace(ctypes.byref(s), hq, k_max, s_max), q.device,
+                    workspace)
+    rc = lib.sparse_decode_attend_sampled(ctypes.byref(s), _ptr(q), hq, _ptr(idx), _ptr(k_per_seq), k_max,
+                                          _ptr(sample), _ptr(sample_weight), _ptr(s_per_seq), s_max,
+                                          float(softmax_scale), _ptr(out), _ptr(ws), ws.numel() * ws.element_size(),
+                                          _stream(stream))
+    if rc != SDI_OK:
+        raise SparseDecodeError(rc, "sparse_decode_attend_sampled")
+    return out

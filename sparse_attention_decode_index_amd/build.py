@@ -9,7 +9,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 LIB_PATH = os.path.join(HERE, "libsparse_decode.so")
-SOURCES = ["api.hip", "index_topk.hip", "attend.hip", "dense.hip", "quest.hip", "labels.hip"]
+SOURCES = ["api.hip", "index_topk.hip", "attend.hip", "dense.hip", "quest.hip", "labels.hip", "sample.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

@@ -103,6 +103,46 @@ int dense_decode(const sdi_kv *kv, const void *q, int32_t num_q_heads, float sof
     return hip_status(sdi::launch_dense(a, (hipStream_t)stream));
 }
 
+int sparse_decode_sample_residual(const sdi_kv *kv, int32_t num_q_heads, const int32_t *idx,
+                                  const int32_t *k_per_seq, int32_t k_max, const uint32_t *draws,
+                                  const int32_t *s_per_seq, int32_t s_max, int32_t *sample_out, float *weight_out,
+                                  void *stream)
+{
+    int rc = check_kv(kv, false);
+    if (rc) return rc;
+    if (!idx || !k_per_seq || !draws || !s_per_seq || !sample_out || !weight_out) return SDI_ERR_NULL;
+    if ((rc = check_heads(kv, num_q_heads))) return rc;
+    if (k_max < 1 || s_max < 1) return SDI_ERR_K;
+    sdi::SampleArgs a{kv->seq_lens, kv->batch, num_q_heads, idx, k_per_seq, k_max, draws, s_per_seq, s_max,
+                      sample_out, weight_out};
+    return hip_status(sdi::launch_sample(a, (hipStream_t)stream));
+}
+
+size_t sparse_decode_attend_sampled_workspace(const sdi_kv *kv, int32_t num_q_heads, int32_t k_max, int32_t s_max)
+{
+    if (!kv || kv->batch < 1 || num_q_heads < 1 || k_max < 1 || s_max < 1 || k_max > INT_MAX - s_max) return 0;
+    return sdi::attend_workspace_bytes(kv->batch, num_q_heads, k_max + s_max);
+}
+
+int sparse_decode_attend_sampled(const sdi_kv *kv, const void *q, int32_t num_q_heads, const int32_t *idx,
+                                 const int32_t *k_per_seq, int32_t k_max, const int32_t *sample,
+                                 const float *sample_weight, const int32_t *s_per_seq, int32_t s_max,
+                                 float softmax_scale, float *out, void *ws, size_t ws_bytes, void *stream)
+{
+    int rc = check_kv(kv, true);
+    if (rc) return rc;
+    if (!q || !idx || !sample || !sample_weight || !out) return SDI_ERR_NULL;
+    if ((rc = check_heads(kv, num_q_heads))) return rc;
+    if (k_max < 1 || s_max < 1 || k_max > INT_MAX / 2 - s_max) return SDI_ERR_K;
+    const size_t need = sparse_decode_attend_sampled_workspace(kv, num_q_heads, k_max, s_max);
+    if (need > 0 && !ws) return SDI_ERR_NULL;
+    if (ws_bytes < need) return SDI_ERR_WORKSPACE;
+    sdi::AttendArgs a{kv->k_cache, kv->v_cache, kv->page_table, kv->seq_lens, kv->batch, kv->num_kv_heads,
+                      kv->max_pages_per_seq, kv->n_max, q, num_q_heads, idx, k_per_seq, k_max, softmax_scale,
+                      out, ws, sample, sample_weight, s_per_seq, s_max};
+    return hip_status(sdi::launch_attend(a, (hipStream_t)stream));
+}
+
 size_t sparse_decode_label_bytes(const sdi_kv *kv)
 {
     if (!kv || kv->num_pages < 1 || kv->num_kv_heads < 1) return 0;
@@ -184,7 +224,7 @@ const char *sparse_decode_strerror(int code)
     case SDI_OK: return "ok";
     case SDI_ERR_NULL: return "a required pointer is NULL";
     case SDI_ERR_SHAPE: return "unsupported shape (head_dim must be 128, page_size 16, q heads a multiple of kv heads, sizes >= 1)";
-    case SDI_ERR_K: return "k_max (or pages_max) must be at least 1";
+    case SDI_ERR_K: return "k_max (or pages_max, s_max) must be at least 1";
     case SDI_ERR_WORKSPACE: return "workspace smaller than the size the *_workspace() query returns";
     case SDI_ERR_HIP: return "a HIP kernel launch failed";
     default: return "unknown sparse_decode status";

@@ -17,6 +17,13 @@
 // 128-bit load per lane for K and one for V); 8 (wide workgroups) or all 16 (chunks)
 // rows of a group are in flight at once, and each group keeps its own running
 // softmax state; the 4 groups, then the W waves, are merged at the end.
+//
+// Two-list mode (stochastic selection): row (b, h) lists its first k'_b = min(k_b,
+// k_max) top-k entries followed by its first s'_b = min(s_b, s_max) drawn entries, and
+// every drawn entry carries the row's weight w (the number of residual tokens each
+// draw stands for).  The weight enters as log2(w) added to the entry's base-2 logit,
+// so w e^{l} is what the softmax sums see.  Chunks past k'_b + s'_b do no work and
+// are not merged, as chunks past k'_b are in the one-list mode.
 #include "sdi_device.hpp"
 #include "sdi_launch.hpp"
 
@@ -38,14 +45,15 @@ int attend_waves(int k_max)
 constexpr float kLog2e = 1.4426950408889634f;
 
 // grid (splits, num_q_heads, batch); 64 W threads, W <= MAXW; BATCH rows per 16-lane
-// group are loaded at once (16 = all of them).
-template <int MAXW, int BATCH>
+// group are loaded at once (16 = all of them).  SAMPLED: two-list mode.
+template <int MAXW, int BATCH, bool SAMPLED>
 __global__ __launch_bounds__(MAXW * 64) void attend_kernel(
     const uint16_t *__restrict__ kc, const uint16_t *__restrict__ vc, const int32_t *__restrict__ page_table,
     const int32_t *__restrict__ seq_lens, const uint16_t *__restrict__ q, const int32_t *__restrict__ idx,
     const int32_t *__restrict__ k_per_seq, int num_q_heads, int num_kv_heads, int group, int max_pages, int k_max,
     float scale_log2, int splits, float *__restrict__ part_ml, float *__restrict__ part_acc,
-    float *__restrict__ out)
+    float *__restrict__ out, const int32_t *__restrict__ sample, const float *__restrict__ sample_weight,
+    const int32_t *__restrict__ s_per_seq, int s_max)
 {
     __shared__ float red_acc[MAXW][kHeadDim];
     __shared__ float red_ml[MAXW][2];
@@ -56,8 +64,10 @@ __global__ __launch_bounds__(MAXW * 64) void attend_kernel(
     const int n = seq_lens[b];
     int kk = k_per_seq ? min(k_per_seq[b], k_max) : k_max;
     if (kk < 0) kk = 0;
+    int len = kk;                            // entries of this row
+    if (SAMPLED) len += max(s_per_seq ? min(s_per_seq[b], s_max) : s_max, 0);
     const int i0 = split * waves * kAttPerWave;
-    if (i0 >= kk) {                          // nothing listed in this chunk
+    if (i0 >= len) {                         // nothing listed in this chunk
         if (splits == 1)
             for (int t = threadIdx.x; t < kHeadDim; t += blockDim.x) out[bh * kHeadDim + t] = 0.f;
         return;                              // (chunks past k are never merged)
@@ -73,16 +83,22 @@ __global__ __launch_bounds__(MAXW * 64) void attend_kernel(
         for (int d = 0; d < 8; ++d) qf[d] *= scale_log2;
     }
 
-    // Each lane resolves one index of the wave's 64 to a cache row number (-1 = skip).
+    // Each lane resolves one index of the wave's 64 to a cache row number (-1 = skip);
+    // in two-list mode also to its base-2 log weight (0 for top-k entries).
     int my_row = -1;
+    float my_lw = 0.f;
     {
         const int i = i0 + wave * kAttPerWave + lane;
+        int j = -1;
         if (i < kk) {
-            const int j = idx[bh * k_max + i];
-            if (j >= 0 && j < n) {
-                const int page = page_table[(int64_t)b * max_pages + (j >> 4)];
-                my_row = (page * num_kv_heads + g) * kPage + (j & 15);
-            }
+            j = idx[bh * k_max + i];
+        } else if (SAMPLED && i < len) {
+            j = sample[bh * s_max + (i - kk)];
+            my_lw = log2f(sample_weight[bh]);
+        }
+        if (j >= 0 && j < n) {
+            const int page = page_table[(int64_t)b * max_pages + (j >> 4)];
+            my_row = (page * num_kv_heads + g) * kPage + (j & 15);
         }
     }
 
@@ -94,9 +110,11 @@ __global__ __launch_bounds__(MAXW * 64) void attend_kernel(
     for (int r0 = 0; r0 < kAttPerWave / 4; r0 += BATCH) {
         u32x4 kw[BATCH], vw[BATCH];
         int rows[BATCH];
+        float lws[BATCH];
 #pragma unroll
         for (int r = 0; r < BATCH; ++r) {
             rows[r] = __shfl(my_row, (r0 + r) * 4 + grp, 64);
+            lws[r] = SAMPLED ? __shfl(my_lw, (r0 + r) * 4 + grp, 64) : 0.f;
             kw[r] = u32x4{0u, 0u, 0u, 0u};
             vw[r] = u32x4{0u, 0u, 0u, 0u};
             if (rows[r] >= 0) {
@@ -115,7 +133,7 @@ __global__ __launch_bounds__(MAXW * 64) void attend_kernel(
 #pragma unroll
             for (int d = 0; d < 8; ++d) s = fmaf(qf[d], kf[d], s);
             s = row16_sum(s);
-            x[r] = rows[r] >= 0 ? s : -INFINITY;
+            x[r] = rows[r] >= 0 ? (SAMPLED ? s + lws[r] : s) : -INFINITY;
             bmax = fmaxf(bmax, x[r]);
         }
         const float m_new = fmaxf(m, bmax);
@@ -179,8 +197,8 @@ __global__ __launch_bounds__(MAXW * 64) void attend_kernel(
 }
 
 // Log-sum-exp merge of per-chunk partials (m, l, acc[128]) of each (b, h).
-// live chunks = ceil(count / per_chunk) with count = min(k_b, k_max) (sparse) or N_b
-// (dense).  grid (num_q_heads, batch); 512 threads: the chunk weights
+// live chunks = ceil(count / per_chunk) with count = min(k_b, k_max) (sparse), N_b
+// (dense), or min(k_b, k_max) + min(s_b, s_max) (two-list mode: counts2 = s_b).  grid (num_q_heads, batch); 512 threads: the chunk weights
 // e^{m_s - M} are computed once into LDS, then 4 groups of 128 threads (one dim
 // each) sum over interleaved chunks and combine their sums in LDS.
 constexpr int kMergeThreads = 512;
@@ -190,7 +208,8 @@ constexpr int kMergeWeights = 4096;                       // chunk weights kept 
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float *__restrict__ part_ml,
                                                               const float *__restrict__ part_acc, int splits,
                                                               int per_chunk, const int32_t *__restrict__ counts,
-                                                              int count_cap, int num_q_heads, float *__restrict__ out)
+                                                              int count_cap, const int32_t *__restrict__ counts2,
+                                                              int count_cap2, int num_q_heads, float *__restrict__ out)
 {
     __shared__ float wts[kMergeWeights];
     __shared__ float red[kMergeThreads / 64];
@@ -200,6 +219,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const float *__res
     const int64_t bh = (int64_t)b * num_q_heads + h;
     int cnt = counts ? min(counts[b], count_cap) : count_cap;
     if (cnt < 0) cnt = 0;
+    if (count_cap2 > 0) cnt += max(counts2 ? min(counts2[b], count_cap2) : count_cap2, 0);
     const int live = min(splits, (cnt + per_chunk - 1) / per_chunk);
     const float *ml = part_ml + bh * splits * 2;
 
@@ -261,36 +281,45 @@ size_t attend_workspace_bytes(int batch, int num_q_heads, int k_max)
 
 hipError_t launch_merge(const float *part_ml, const float *part_acc, int splits, int per_chunk,
                         const int32_t *counts, int count_cap, int batch, int num_q_heads, float *out,
-                        hipStream_t stream)
+                        hipStream_t stream, const int32_t *counts2, int count_cap2)
 {
     hipLaunchKernelGGL(merge_kernel, dim3(num_q_heads, batch), dim3(kMergeThreads), 0, stream, part_ml, part_acc,
-                       splits, per_chunk, counts, count_cap, num_q_heads, out);
+                       splits, per_chunk, counts, count_cap, counts2, count_cap2, num_q_heads, out);
     return hipGetLastError();
+}
+
+template <bool SAMPLED>
+static hipError_t launch_attend_mode(const AttendArgs &a, hipStream_t stream)
+{
+    const int group = a.num_q_heads / a.num_kv_heads;
+    const int total = SAMPLED ? a.k_max + a.s_max : a.k_max;   // entries of a row
+    const int splits = attend_splits(total);
+    const size_t bhs = (size_t)a.batch * a.num_q_heads * splits;
+    float *part_acc = (float *)a.ws;
+    float *part_ml = splits > 1 ? part_acc + bhs * kHeadDim : nullptr;
+    const int waves = attend_waves(total);
+    const dim3 grid(splits, a.num_q_heads, a.batch);
+    if (total <= kAttWideMax)
+        hipLaunchKernelGGL((attend_kernel<kAttMaxWaves, 8, SAMPLED>), grid, dim3(waves * 64), 0, stream,
+                           (const uint16_t *)a.k_cache, (const uint16_t *)a.v_cache, a.page_table, a.seq_lens,
+                           (const uint16_t *)a.q, a.idx, a.k_per_seq, a.num_q_heads, a.num_kv_heads, group,
+                           a.max_pages, a.k_max, a.scale * kLog2e, splits, part_ml, part_acc, a.out, a.sample,
+                           a.sample_weight, a.s_per_seq, a.s_max);
+    else
+        hipLaunchKernelGGL((attend_kernel<kAttChunkWaves, 16, SAMPLED>), grid, dim3(waves * 64), 0, stream,
+                           (const uint16_t *)a.k_cache, (const uint16_t *)a.v_cache, a.page_table, a.seq_lens,
+                           (const uint16_t *)a.q, a.idx, a.k_per_seq, a.num_q_heads, a.num_kv_heads, group,
+                           a.max_pages, a.k_max, a.scale * kLog2e, splits, part_ml, part_acc, a.out, a.sample,
+                           a.sample_weight, a.s_per_seq, a.s_max);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || splits == 1) return e;
+    return launch_merge(part_ml, part_acc, splits, waves * kAttPerWave, a.k_per_seq, a.k_max, a.batch,
+                        a.num_q_heads, a.out, stream, SAMPLED ? a.s_per_seq : nullptr, SAMPLED ? a.s_max : 0);
 }
 
 hipError_t launch_attend(const AttendArgs &a, hipStream_t stream)
 {
-    const int group = a.num_q_heads / a.num_kv_heads;
-    const int splits = attend_splits(a.k_max);
-    const size_t bhs = (size_t)a.batch * a.num_q_heads * splits;
-    float *part_acc = (float *)a.ws;
-    float *part_ml = splits > 1 ? part_acc + bhs * kHeadDim : nullptr;
-    const int waves = attend_waves(a.k_max);
-    const dim3 grid(splits, a.num_q_heads, a.batch);
-    if (a.k_max <= kAttWideMax)
-        hipLaunchKernelGGL((attend_kernel<kAttMaxWaves, 8>), grid, dim3(waves * 64), 0, stream,
-                           (const uint16_t *)a.k_cache, (const uint16_t *)a.v_cache, a.page_table, a.seq_lens,
-                           (const uint16_t *)a.q, a.idx, a.k_per_seq, a.num_q_heads, a.num_kv_heads, group,
-                           a.max_pages, a.k_max, a.scale * kLog2e, splits, part_ml, part_acc, a.out);
-    else
-        hipLaunchKernelGGL((attend_kernel<kAttChunkWaves, 16>), grid, dim3(waves * 64), 0, stream,
-                           (const uint16_t *)a.k_cache, (const uint16_t *)a.v_cache, a.page_table, a.seq_lens,
-                           (const uint16_t *)a.q, a.idx, a.k_per_seq, a.num_q_heads, a.num_kv_heads, group,
-                           a.max_pages, a.k_max, a.scale * kLog2e, splits, part_ml, part_acc, a.out);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess || splits == 1) return e;
-    return launch_merge(part_ml, part_acc, splits, waves * kAttPerWave, a.k_per_seq, a.k_max, a.batch,
-                        a.num_q_heads, a.out, stream);
+    return a.sample ? launch_attend_mode<true>(a, stream) : launch_attend_mode<false>(a, stream);
 }
 
 }  // namespace sdi

@@ -31,7 +31,6 @@ namespace sdi {
 
 constexpr int kLabelRowElems = kLabelDims;                    // bf16 per label row
 constexpr int kLabelPageElems = kPage * kLabelDims;           // 512 B per (page, kv head)
-constexpr int kLblPerThread = kScoreTokensPerBlock / (kScoreWaves * 64);   // 8 tokens per thread
 
 // grid (ceil(pages / 4), Hkv, B) or (1, Hkv, B) for the current pages only; 256 threads,
 // one wave per page: lane (row, part) gathers channels 4 part .. 4 part + 3 of a row.

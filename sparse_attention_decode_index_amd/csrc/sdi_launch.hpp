@@ -34,6 +34,24 @@ struct AttendArgs {
     float scale;
     float *out;
     void *ws;
+    // two-list mode (stochastic selection): drawn tokens [B][Hq][s_max], weight [B][Hq],
+    // draws per sequence [B] (NULL: s_max)
+    const int32_t *sample = nullptr;
+    const float *sample_weight = nullptr;
+    const int32_t *s_per_seq = nullptr;
+    int s_max = 0;
+};
+
+struct SampleArgs {
+    const int32_t *seq_lens;
+    int batch, num_q_heads;
+    const int32_t *idx, *k_per_seq;   // top-k rows [B][Hq][k_max]
+    int k_max;
+    const uint32_t *draws;            // [B][Hq][s_max]
+    const int32_t *s_per_seq;
+    int s_max;
+    int32_t *sample_out;              // [B][Hq][s_max]
+    float *weight_out;                // [B][Hq]
 };
 
 struct QuestArgs {
@@ -70,10 +88,11 @@ hipError_t launch_index_topk(const IndexArgs &a, hipStream_t stream);
 int attend_splits(int k_max);
 size_t attend_workspace_bytes(int batch, int num_q_heads, int k_max);
 hipError_t launch_attend(const AttendArgs &a, hipStream_t stream);
+hipError_t launch_sample(const SampleArgs &a, hipStream_t stream);
 
 hipError_t launch_merge(const float *part_ml, const float *part_acc, int splits, int per_chunk,
                         const int32_t *counts, int count_cap, int batch, int num_q_heads, float *out,
-                        hipStream_t stream);
+                        hipStream_t stream, const int32_t *counts2 = nullptr, int count_cap2 = 0);
 
 size_t label_bytes(int num_pages, int num_kv_heads);
 hipError_t launch_label_build(const LabelArgs &a, int last_only, hipStream_t stream);

@@ -169,6 +169,39 @@ def test_label_sizes_and_errors(lib):
     assert idx(nbytes=need - 1) == sdi.SDI_ERR_WORKSPACE
 
 
+def test_sample_sizes_and_errors(lib):
+    k = kv()
+    # two-list rows of k_max + s_max entries: one workgroup up to 1024, 256-entry chunks beyond
+    assert lib.sparse_decode_attend_sampled_workspace(ctypes.byref(k), 8, 600, 424) == 0
+    assert lib.sparse_decode_attend_sampled_workspace(ctypes.byref(k), 8, 600, 425) == 2 * 8 * 5 * 130 * 4
+    assert lib.sparse_decode_attend_sampled_workspace(ctypes.byref(k), 8, 600, 0) == 0
+
+    def smp(hq=8, idx=FAKE, kps=FAKE, k_max=5, draws=FAKE, sps=FAKE, s_max=7, out=FAKE, w=FAKE, kvv=k):
+        return lib.sparse_decode_sample_residual(ctypes.byref(kvv), hq, idx, kps, k_max, draws, sps, s_max, out, w,
+                                                 None)
+    for over in (dict(idx=None), dict(kps=None), dict(draws=None), dict(sps=None), dict(out=None), dict(w=None)):
+        assert smp(**over) == sdi.SDI_ERR_NULL
+    assert smp(hq=3) == sdi.SDI_ERR_SHAPE
+    assert smp(kvv=kv(head_dim=64)) == sdi.SDI_ERR_SHAPE
+    assert smp(k_max=0) == sdi.SDI_ERR_K
+    assert smp(s_max=0) == sdi.SDI_ERR_K
+
+    def att(hq=8, q=FAKE, idx=FAKE, kps=FAKE, k_max=600, sm=FAKE, w=FAKE, s_max=500, out=FAKE, ws=FAKE,
+            nbytes=1 << 40):
+        return lib.sparse_decode_attend_sampled(ctypes.byref(k), q, hq, idx, kps, k_max, sm, w, FAKE, s_max,
+                                                ctypes.c_float(0.1), out, ws, nbytes, None)
+    for over in (dict(q=None), dict(idx=None), dict(sm=None), dict(w=None), dict(out=None), dict(ws=None)):
+        assert att(**over) == sdi.SDI_ERR_NULL
+    assert att(hq=5) == sdi.SDI_ERR_SHAPE
+    assert att(s_max=0) == sdi.SDI_ERR_K
+    assert att(k_max=0) == sdi.SDI_ERR_K
+    need = lib.sparse_decode_attend_sampled_workspace(ctypes.byref(k), 8, 600, 500)
+    assert att(nbytes=need - 1) == sdi.SDI_ERR_WORKSPACE
+    assert lib.sparse_decode_attend_sampled(ctypes.byref(kv(v_cache=None)), FAKE, 8, FAKE, FAKE, 600, FAKE, FAKE,
+                                            FAKE, 500, ctypes.c_float(0.1), FAKE, FAKE, 1 << 40,
+                                            None) == sdi.SDI_ERR_NULL
+
+
 def test_missing_library_fails_loudly(tmp_path):
     with pytest.raises(ImportError):
         sdi.load_library(str(tmp_path / "libsparse_decode.so"))
