@@ -51,6 +51,7 @@ namespace sdi {
 constexpr int kScoreUnroll = 2;                               // pages per register buffer (a group)
 constexpr int kScoreBufs = 2;                                 // groups in flight per wave (3 measured no faster)
 constexpr int kSlotGroups = kScorePagesPerWave / kScoreUnroll;
+constexpr int kGatherUnroll = 4;                              // candidates in flight per select thread
 constexpr int kStageRow = kRowBytes + 16;                     // padded LDS row: conflict-free both ways
 constexpr int kStagePage = kPage * kStageRow;                 // 4352 B
 constexpr int kSubCap = kCandCap / 4;                         // ... as 4 lane lists (one per quad) of 48
@@ -489,32 +490,32 @@ __global__ __launch_bounds__(kScoreWaves * 64, 2) void score_kernel(
 
 // ---- 2. select ---------------------------------------------------------------------------
 
-// Candidate keys gathered into LDS in token order.  The candidates of slot i are
-// positions [first[i], first[i + 1]); blk[v / 64] is the slot of position 64 (v / 64),
-// where the walk to position v's slot starts.  A token is found from its slot's record.
+// Candidate keys and their in-slot positions gathered into LDS in token order.  The
+// candidates of slot i are positions [first[i], first[i + 1]); blk[v / 64] is the
+// slot of position 64 (v / 64), where the walk to position v's slot starts.
+__device__ __forceinline__ int slot_of_position(const uint32_t *first, const uint32_t *blk, uint32_t v)
+{
+    int i = (int)blk[v >> 6];
+    while (v >= first[i + 1]) ++i;
+    return i;
+}
+
 struct LdsCandidates {
     const uint32_t *key, *first, *blk;
-    const uint32_t *rec_row;                                  // the row's slot records
+    const uint16_t *pos;                                      // token - slot start, per position
     __device__ int load8(int start, int n, uint32_t (&v)[8]) const { return load_keys8(key, start, n, v); }
     // tokens of positions start .. start + cnt - 1 (cnt <= 8, all below the total)
     __device__ void tokens8(int start, int cnt, int32_t (&t)[8]) const
     {
         int i = (int)blk[start >> 6];
-        uint32_t f0 = first[i], f1 = first[i + 1];
-        int slot_of[8], j_of[8];
+        uint32_t f1 = first[i + 1];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const uint32_t v = (uint32_t)(start + e);
             if (e < cnt) {
-                while (v >= f1) { ++i; f0 = f1; f1 = first[i + 1]; }
+                while (v >= f1) { ++i; f1 = first[i + 1]; }
             }
-            slot_of[e] = i;
-            j_of[e] = e < cnt ? (int)(v - f0) : 0;
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const uint16_t *pos = (const uint16_t *)(rec_row + (int64_t)slot_of[e] * kRecWords + kCandCap + 4);
-            t[e] = e < cnt ? slot_of[e] * kWaveTokens + pos[j_of[e]] : -1;
+            t[e] = e < cnt ? i * kWaveTokens + pos[v] : -1;
         }
     }
 };
@@ -568,7 +569,8 @@ __device__ __forceinline__ void select_rescore_generic(const SelectArgs &a, int6
 // grid (num_q_heads, batch); kSelThreads threads; dynamic LDS holds the candidates.
 __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a)
 {
-    extern __shared__ __attribute__((aligned(16))) uint32_t dyn_lds[];   // keys[cap] | first[slots + 1] | blk
+    // keys[cap] | first[slots + 1] | blk[cap / 64] | positions (16-bit) [cap]
+    extern __shared__ __attribute__((aligned(16))) uint32_t dyn_lds[];
     __shared__ __attribute__((aligned(16))) uint32_t hist[kHistBins];
     __shared__ uint32_t scratch[kSelWaves + 2];
     __shared__ uint32_t res[8];
@@ -594,6 +596,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a)
     }
     bool generic = a.cap == 0;
     uint32_t *ckey = dyn_lds, *first = dyn_lds + a.cap, *blk = first + a.slots + 1;
+    uint16_t *cpos = (uint16_t *)(blk + (a.cap + 63) / 64);
     const int nslots = (n + kWaveTokens - 1) / kWaveTokens;
     uint32_t total = 0;
     if (threadIdx.x < 8) res[threadIdx.x] = 0u;
@@ -642,39 +645,42 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a)
         select_rescore_generic(a, bh, b, h, n, kk, hist, scratch, res, out);
         return;
     }
-    // 2. gather the candidate keys into LDS in token order, one thread per slot (its
-    //    list in 16-byte pieces, all in flight), counting the first radix digit of
-    //    d = key - lo on the way.  lo is the largest bound: a key below it can never be
-    //    selected (T must reach every bound), so such keys stay in place but take no
-    //    part in the digits; a workgroup that kept all its tokens (bound 0, a row's
-    //    short tail) then does not stretch the digits over the whole key range.  The
-    //    largest candidate key gives the digits' span (bits).
+    // 2. gather the candidates into LDS in token order: thread t takes list positions
+    //    t, t + 512, ... (kGatherUnroll of them in flight at once), finds each one's
+    //    slot, and loads its key and its 16-bit position from the slot's record; the
+    //    first radix digit of d = key - lo is counted on the way.  lo is the largest
+    //    bound: a key below it can never be selected (T must reach every bound), so
+    //    such keys stay in place but take no part in the digits; a workgroup that kept
+    //    all its tokens (bound 0, a row's short tail) then does not stretch the digits
+    //    over the whole key range.  The largest candidate key gives the digits' span.
     const uint32_t lo = res[6], lo_max = lo, hi_max = res[7];
     const int bits = hi_max >= lo ? 32 - __clz((int)(hi_max - lo)) : 0;
     const int w0 = min(12, bits), sh0 = bits - w0;
     const uint32_t mask0 = (1u << w0) - 1u;
     uint32_t eligible = 0;                                    // keys >= lo this thread gathered
-    for (int i = threadIdx.x; i < nslots; i += kSelThreads) {
-        const uint32_t p0 = first[i], c = first[i + 1] - p0;
-        const uint32_t *keys = rec_row + (int64_t)i * kRecWords;
-        for (uint32_t j0 = 0; j0 < c; j0 += 32) {
-            u32x4 k4[8];
+    for (uint32_t v0 = 0; v0 < total; v0 += kSelThreads * kGatherUnroll) {
+        uint32_t key[kGatherUnroll];
+        uint16_t ps[kGatherUnroll];
 #pragma unroll
-            for (int u = 0; u < 8; ++u)
-                if (j0 + 4 * u < c) k4[u] = *(const u32x4 *)(keys + j0 + 4 * u);
+        for (int u = 0; u < kGatherUnroll; ++u) {
+            const uint32_t v = v0 + u * kSelThreads + threadIdx.x;
+            if (v < total) {
+                const int i = slot_of_position(first, blk, v);
+                const uint32_t *rec = rec_row + (int64_t)i * kRecWords;
+                const uint32_t j = v - first[i];
+                key[u] = rec[j];
+                ps[u] = ((const uint16_t *)(rec + kCandCap + 4))[j];
+            }
+        }
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const uint32_t j = j0 + 4 * u + e;
-                    if (j < c) {
-                        const uint32_t key = k4[u][e];
-                        ckey[p0 + j] = key;
-                        if (key >= lo) {
-                            ++eligible;
-                            if (bits > 0) atomicAdd(&hist[((key - lo) >> sh0) & mask0], 1u);
-                        }
-                    }
+        for (int u = 0; u < kGatherUnroll; ++u) {
+            const uint32_t v = v0 + u * kSelThreads + threadIdx.x;
+            if (v < total) {
+                ckey[v] = key[u];
+                cpos[v] = ps[u];
+                if (key[u] >= lo) {
+                    ++eligible;
+                    if (bits > 0) atomicAdd(&hist[((key[u] - lo) >> sh0) & mask0], 1u);
                 }
             }
         }
@@ -693,7 +699,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a)
     //    already reaches every bound, the bin floor is T with all ties; otherwise the
     //    bin's few entries are ranked exactly by one wave.  The selection is valid if T
     //    reaches every workgroup bound.
-    const LdsCandidates cands{ckey, first, blk, rec_row};
+    const LdsCandidates cands{ckey, first, blk, cpos};
     uint32_t T = lo, r = (uint32_t)kk;
     if (bits > 0) {
         threshold_bin_wave(hist, max(64, 1 << w0), (uint32_t)kk, res);
@@ -765,9 +771,9 @@ SelectPlan plan_select(int k_max, int n_max, int slots)
     // (15% margin).  Rows beyond the capacity take the re-scoring path.
     const double kd = k_max, nd = n_max;
     const double expect = kd + 6.0 * std::sqrt(kd * nd / 1024.0) + 8.0 * nd / 1024.0;
-    // Beside the keys, the slot starts take (slots + 1) words and the walk starts one
-    // word per 64 keys.
-    const int cap_lds = ((int)(kSelDynMax / sizeof(uint32_t)) - (slots + 2)) * 64 / 65;
+    // Beside the keys, the slot starts take (slots + 1) words, the walk starts one word
+    // per 64 keys and the positions half a word per key.
+    const int cap_lds = ((int)(kSelDynMax / sizeof(uint32_t)) - (slots + 3)) * 128 / 194;
     const int cap_want = (int)std::min<double>(1e9, std::ceil(1.15 * expect) + 256.0);
     int cap = std::max(0, std::min(std::min(cap_want, kSelCapMax), cap_lds));
     // A large k (or a row too long for the slot table) would overflow the slot lists or
@@ -780,7 +786,9 @@ SelectPlan plan_select(int k_max, int n_max, int slots)
     const double mu = 1024.0 * kd / nd, r = mu + 6.0 * std::sqrt(mu) + 8.0;
     const bool all_keys = cap_want > cap || r / 2.0 > kSlotExpectMax;
     if (all_keys) cap = 0;
-    const size_t dyn = cap == 0 ? 0 : (size_t)(cap + slots + 1 + (cap + 63) / 64) * sizeof(uint32_t);
+    const size_t dyn = cap == 0 ? 0
+                                : (size_t)(cap + slots + 1 + (cap + 63) / 64) * sizeof(uint32_t) +
+                                      (size_t)(cap + 1) / 2 * sizeof(uint32_t);
     return SelectPlan{cap, dyn, all_keys};
 }
 
