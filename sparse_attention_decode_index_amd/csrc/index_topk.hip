@@ -26,7 +26,7 @@
 //                    streaming speed.
 //  2. select_kernel  per (b, h): the slot counts give each candidate's place, the
 //                    candidates are gathered into LDS in token order, radix passes
-//                    over key - min(lo) (12 bits at a time, usually two) find the
+//                    over key - min(lo) (kHistBits at a time, usually two) find the
 //                    exact k-th key T and an ordered compaction writes the row.
 //
 // Exactness does not depend on the sample: if T, the k'-th largest candidate key,
@@ -655,7 +655,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a)
     //    over the whole key range.  The largest candidate key gives the digits' span.
     const uint32_t lo = res[6], lo_max = lo, hi_max = res[7];
     const int bits = hi_max >= lo ? 32 - __clz((int)(hi_max - lo)) : 0;
-    const int w0 = min(12, bits), sh0 = bits - w0;
+    const int w0 = min(kHistBits, bits), sh0 = bits - w0;
     const uint32_t mask0 = (1u << w0) - 1u;
     uint32_t eligible = 0;                                    // keys >= lo this thread gathered
     for (uint32_t v0 = 0; v0 < total; v0 += kSelThreads * kGatherUnroll) {

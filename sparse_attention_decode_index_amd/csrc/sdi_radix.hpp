@@ -97,7 +97,7 @@ __device__ __forceinline__ void compact_selected(const Src &src, int n, int kk, 
                                                  uint32_t *scratch, int32_t *__restrict__ out);
 
 // Exact selection over n keys in token order, every key >= base: radix passes over
-// the digits of d = key - base (d < 2^bits), 12 bits at a time from the top, find
+// the digits of d = key - base (d < 2^bits), kHistBits at a time from the top, find
 // the kk-th largest key T and how many keys equal to T to take (the first ones,
 // i.e. the lowest tokens); one ordered-compaction pass then writes the selected
 // tokens ascending and pads the row with -1.  Returns false, writing nothing, if
@@ -113,7 +113,7 @@ __device__ __forceinline__ bool radix_select(const Src &src, int n, int kk, int 
     bool ready = first_hist_ready;                           // the caller built the first digit's histogram
 #pragma unroll 1
     while (hi > 0) {
-        const int w = min(12, hi), lo = hi - w, nb = max(64, 1 << w);
+        const int w = min(kHistBits, hi), lo = hi - w, nb = max(64, 1 << w);
         if (!ready) {
             for (int i = threadIdx.x; i < nb; i += kSelThreads) hist[i] = 0u;
             if (threadIdx.x == 0) { res[0] = 0u; res[1] = 0u; }
