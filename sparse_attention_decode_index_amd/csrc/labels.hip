@@ -56,12 +56,15 @@ __global__ __launch_bounds__(256) void label_build_kernel(const uint16_t *__rest
         uint2{v[0] | (v[1] << 16), v[2] | (v[3] << 16)};
 }
 
-// grid (ceil(n_max / 2048), Hkv * head_blocks, B); 256 threads, three workgroups per CU.
-// Wave w owns the workgroup's slot w (tokens 512 w .. 512 w + 511), lane l its tokens
-// 512 w + 64 i + l, i = 0..7: it scores them, keeps their keys in registers for the
-// records, and shares only their 16-bit codes (for the workgroup's bound) in LDS.
-template <bool kAllKeys>
-__global__ __launch_bounds__(kScoreWaves * 64, 3) void label_score_kernel(
+// grid (ceil(n_max / 2048), Hkv * head_blocks, B); 256 threads; up to kHeads q heads
+// per workgroup.  Wave w owns the workgroup's slot w (tokens 512 w .. 512 w + 511),
+// lane l its tokens 512 w + 64 i + l, i = 0..7: it scores them, keeps their keys in
+// registers for the records, and shares only their 16-bit codes (for the workgroup's
+// bound) in LDS.  A group of at most four heads takes the four-head form: half the key
+// registers, so four workgroups fit a CU instead of three, and a layer whose
+// workgroups number four per CU runs in one round.
+template <bool kAllKeys, int kHeads>
+__global__ __launch_bounds__(kScoreWaves * 64, kHeads <= 4 ? 4 : 3) void label_score_kernel(
     const uint16_t *__restrict__ labels, const int32_t *__restrict__ page_table,
     const int32_t *__restrict__ seq_lens, const uint16_t *__restrict__ q, const int32_t *__restrict__ k_per_seq,
     const int32_t *__restrict__ channels, int num_q_heads, int num_kv_heads, int group, int head_blocks,
@@ -69,17 +72,17 @@ __global__ __launch_bounds__(kScoreWaves * 64, 3) void label_score_kernel(
     int64_t key_stride)
 {
     constexpr int kPer = kWaveTokens / 64;                    // 8 tokens per lane
-    __shared__ __attribute__((aligned(16))) uint16_t codes[kHeadBlock][kScoreTokensPerBlock];   // 32 KB
-    __shared__ __attribute__((aligned(16))) float qc_lds[kHeadBlock][kLabelDims];
-    __shared__ uint32_t lo_lds[kHeadBlock];
+    __shared__ __attribute__((aligned(16))) uint16_t codes[kHeads][kScoreTokensPerBlock];   // 4 KB per head
+    __shared__ __attribute__((aligned(16))) float qc_lds[kHeads][kLabelDims];
+    __shared__ uint32_t lo_lds[kHeads];
     const int b = blockIdx.z;
     const int g = blockIdx.y / head_blocks, hb = blockIdx.y - g * head_blocks;
     const int n = seq_lens[b];
     const int tok0 = blockIdx.x * kScoreTokensPerBlock;
     if (tok0 >= n) return;                                    // whole block exits together
     const int kk = min(min(k_per_seq[b], n), k_max);
-    const int heads_here = min(kHeadBlock, group - hb * kHeadBlock);
-    const int h0 = g * group + hb * kHeadBlock;
+    const int heads_here = min(kHeads, group - hb * kHeads);
+    const int h0 = g * group + hb * kHeads;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int n_wg = min(kScoreTokensPerBlock, n - tok0);     // the workgroup's tokens
     // 1. the lane's 8 label rows in flight (page-table entries, then rows), and the
@@ -109,9 +112,9 @@ __global__ __launch_bounds__(kScoreWaves * 64, 3) void label_score_kernel(
     }
     if (q_lane) qc_lds[qh][qcn] = __uint_as_float(qbits << 16);
     lds_barrier();
-    uint32_t key[kHeadBlock][kPer];
+    uint32_t key[kHeads][kPer];
 #pragma unroll
-    for (int h = 0; h < kHeadBlock; ++h) {
+    for (int h = 0; h < kHeads; ++h) {
         if (h < heads_here) {                                 // uniform
             float qc[kLabelDims];
 #pragma unroll
@@ -126,7 +129,7 @@ __global__ __launch_bounds__(kScoreWaves * 64, 3) void label_score_kernel(
     }
     if constexpr (kAllKeys) {                                 // every key to the head's key row
 #pragma unroll
-        for (int h = 0; h < kHeadBlock; ++h) {
+        for (int h = 0; h < kHeads; ++h) {
             if (h < heads_here) {
                 uint32_t *krow = keys32 + ((int64_t)b * num_q_heads + h0 + h) * key_stride + tok0;
 #pragma unroll
@@ -185,7 +188,7 @@ __global__ __launch_bounds__(kScoreWaves * 64, 3) void label_score_kernel(
         const uint32_t row_bytes = (uint32_t)slots * kRecWords * 4u;
         const uint32_t rec0 = (uint32_t)slot * kRecWords * 4u;
 #pragma unroll
-        for (int h = 0; h < kHeadBlock; ++h) {
+        for (int h = 0; h < kHeads; ++h) {
             if (h < heads_here) {
                 const uint32_t lo = lo_lds[h];
                 const int64_t row_h = (int64_t)b * num_q_heads + h0 + h;
@@ -235,7 +238,8 @@ hipError_t launch_label_build(const LabelArgs &a, int last_only, hipStream_t str
 hipError_t launch_label_index_topk(const LabelArgs &a, hipStream_t stream)
 {
     const int group = a.num_q_heads / a.num_kv_heads;
-    const int head_blocks = (group + kHeadBlock - 1) / kHeadBlock;
+    const int heads = group <= 4 ? 4 : kHeadBlock;             // q heads per workgroup
+    const int head_blocks = (group + heads - 1) / heads;
     const int64_t stride = (int64_t)index_topk_key_stride(a.n_max);
     const int slots = index_topk_slots(a.n_max);
     uint32_t *keys32 = (uint32_t *)a.ws;
@@ -248,8 +252,13 @@ hipError_t launch_label_index_topk(const LabelArgs &a, hipStream_t stream)
                            a.page_table, a.seq_lens, (const uint16_t *)a.q, a.k_per_seq, a.channels, a.num_q_heads,
                            a.num_kv_heads, group, head_blocks, a.max_pages, a.k_max, cand_rec, slots, keys32, stride);
     };
-    if (plan.all_keys) launch_score(label_score_kernel<true>);
-    else launch_score(label_score_kernel<false>);
+    if (heads == 4) {
+        if (plan.all_keys) launch_score(label_score_kernel<true, 4>);
+        else launch_score(label_score_kernel<false, 4>);
+    } else {
+        if (plan.all_keys) launch_score(label_score_kernel<true, kHeadBlock>);
+        else launch_score(label_score_kernel<false, kHeadBlock>);
+    }
     SelectArgs s{(const uint16_t *)a.k_cache, a.page_table, a.seq_lens, a.k_per_seq, (const uint16_t *)a.q,
                  cand_rec, slots, plan.cap, plan.all_keys ? 1 : 0, keys32, stride, a.num_q_heads, a.num_kv_heads,
                  group, a.max_pages, a.k_max, a.idx_out, (const uint16_t *)a.labels, a.channels};
