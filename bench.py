@@ -189,12 +189,12 @@ def calibrate_channels(wl, r=16, sample=2048):
     """Offline channel choice for the label indexer: per kv head the r channels of
     largest mean |K| over the first `sample` tokens of sequence 0 (a calibration
     sample, not the step's data)."""
-    vals = (wl.k_cache.astype(np.uint32) << 16).view(np.float32)
     n = min(sample, int(wl.seq_lens[0]))
     pages = wl.page_table[0, :-(-n // 16)]
+    vals = (wl.k_cache[pages].astype(np.uint32) << 16).view(np.float32)    # only the sample's pages
     ch = np.zeros((wl.num_kv_heads, r), np.int32)
     for g in range(wl.num_kv_heads):
-        rows = vals[pages, g].reshape(-1, 128)[:n]
+        rows = vals[:, g].reshape(-1, 128)[:n]
         ch[g] = np.sort(np.argsort(-np.abs(rows).mean(axis=0), kind="stable")[:r])
     return ch
 

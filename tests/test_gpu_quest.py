@@ -36,6 +36,15 @@ def _pages_of(tokens):
 def check_quest(dev, cache, q, m_per_seq, m_max, strict=False, tag=""):
     print(f"[case] {tag} B={cache.batch} N={list(cache.sl)[:6]} m={list(m_per_seq)[:6]} m_max={m_max}", flush=True)
     summ_t, summ_bits, gtok = dev.quest(m_per_seq, m_max)
+    compare_quest(summ_bits, gtok, cache, q, m_per_seq, m_max, strict, tag)
+    out = dev.attend(gtok)
+    check_close(out, oracle.attend(cache, q, gtok), what=f"{tag} attend(quest tokens)")
+    return gtok, out
+
+
+def compare_quest(summ_bits, gtok, cache, q, m_per_seq, m_max, strict=False, tag=""):
+    """GPU summaries (by physical page) and token lists of the sequences in `cache`
+    against the oracle."""
     sm = oracle.quest_summaries(cache)
     vals = _bf16_values(summ_bits)
     for b in range(cache.batch):
@@ -71,9 +80,6 @@ def check_quest(dev, cache, q, m_per_seq, m_max, strict=False, tag=""):
                 for p in diff:
                     assert abs(u[b, h, p] - thr[b, h]) <= 2 * err.max(), \
                         f"{tag}: b={b} h={h} page {p} bound {u[b, h, p]} vs threshold {thr[b, h]}"
-    out = dev.attend(gtok)
-    check_close(out, oracle.attend(cache, q, gtok), what=f"{tag} attend(quest tokens)")
-    return gtok, out
 
 
 @pytest.mark.parametrize("cfg,kw,m", [
