@@ -122,16 +122,22 @@ def cpu_baseline(wl, target_s):
                       f"{wl.batch} sequences ({total:.1f} s), scaled to the whole batch"}
 
 
-def quest_leg(sdi, wl, kv_full, step_args, timed_graph, per, reps, k_max, idx, out, ws_attend, dense_s):
+def quest_leg(sdi, wl, kv_full, step_args, timed_graph, per, reps, n_q, k_max, idx, out, ws_attend, dense_s):
     """Quest-style step at the exact indexer's token budget: the current pages'
-    summaries refreshed, the page selection (m = ceil(k / 16) pages, current page
-    included), then the gather-attend over those pages' tokens.  Recall = share of
-    the exact top-k tokens (step 0) that the selected pages contain."""
+    summaries refreshed, the page selection (m_b = ceil(k_b / 16) pages, current page
+    included), then the gather-attend over those pages' tokens (16 m_b entries per
+    row).  Recall = share of the exact top-k tokens (step 0) that the selected pages
+    contain."""
     import torch
     dev = idx.device
     B, hq = wl.batch, wl.num_q_heads
     pages_max = (k_max + 15) // 16
-    pps = torch.from_numpy(np.full(B, pages_max, np.int32)).to(dev)
+    budget = {}
+    for j in range(n_q):
+        kps = step_args(j)[2]
+        if id(kps) not in budget:
+            m = (kps + 15) // 16
+            budget[id(kps)] = (m, 16 * m)
     summary = sdi.quest_summarize(kv_full)                   # prefill: every page once
     qidx = torch.empty((B, hq, 16 * pages_max), dtype=torch.int32, device=dev)
     ws_q = torch.empty(max(1, sdi.load_library().sparse_decode_quest_select_workspace(
@@ -144,13 +150,13 @@ def quest_leg(sdi, wl, kv_full, step_args, timed_graph, per, reps, k_max, idx, o
         sdi.quest_summarize(kv, summary, current_pages_only=True, stream=torch.cuda.current_stream())
 
     def select(s):
-        kv, q, _ = step_args(s)
-        sdi.quest_select(kv, q, summary, pps, pages_max, idx_out=qidx, workspace=ws_q,
+        kv, q, kps = step_args(s)
+        sdi.quest_select(kv, q, summary, budget[id(kps)][0], pages_max, idx_out=qidx, workspace=ws_q,
                          stream=torch.cuda.current_stream())
 
     def attend(s):
-        kv, q, _ = step_args(s)
-        sdi.attend(kv, q, qidx, None, out=out, workspace=ws_qa, stream=torch.cuda.current_stream())
+        kv, q, kps = step_args(s)
+        sdi.attend(kv, q, qidx, budget[id(kps)][1], out=out, workspace=ws_qa, stream=torch.cuda.current_stream())
 
     def step(s):
         update(s)
@@ -176,7 +182,7 @@ def quest_leg(sdi, wl, kv_full, step_args, timed_graph, per, reps, k_max, idx, o
             e = ex[b, h][ex[b, h] >= 0]
             if len(e):
                 rec.append(np.isin(e, qt[b, h]).mean())
-    res = {"pages": pages_max, "tokens": 16 * pages_max, "summary_update_us": t_upd * 1e6,
+    res = {"pages_max": pages_max, "tokens_max": 16 * pages_max, "summary_update_us": t_upd * 1e6,
            "select_us": t_sel * 1e6, "attend_us": t_att * 1e6, "step_us": t_step * 1e6,
            "recall_of_exact_topk": float(np.mean(rec)),
            "select_bytes_per_launch": int((wl.num_kv_heads * ((wl.seq_lens.astype(np.int64) + 15) // 16) * 512).sum())}
@@ -490,7 +496,8 @@ def main():
 
     quest = None
     if args.quest and args.mode == "graph":
-        quest = quest_leg(sdi, wl, kv_full, step_args, timed_graph, per, reps, k_max, idx, out, ws_attend, dense_s)
+        quest = quest_leg(sdi, wl, kv_full, step_args, timed_graph, per, reps, n_q, k_max, idx, out, ws_attend,
+                          dense_s)
 
     labels = None
     if args.labels and args.mode == "graph":
