@@ -280,6 +280,23 @@ def test_full_size_sampled(cfg, sample):
     check_close(dn[sub], oracle.dense(cache, q), what=f"C{cfg} dense")
 
 
+def test_long_rows_many_slots():
+    """Rows of more than 512 slots (262144 tokens): the select reads the slot headers in
+    several passes; a 270000-token row beside a 40000-token one, fragmented pages.  The
+    cache is drawn straight into its pages as bf16 bit patterns (random sign and 7-bit
+    mantissa in [0.5, 1); V reuses K's bits, the other tests keep them apart)."""
+    rng = np.random.default_rng(29)
+    lens = np.array([270000, 40000], np.int32)
+    pt, pool = synth.make_page_table("fragmented", 29, lens)
+
+    def draw(*shape):
+        return (rng.integers(0, 1 << 16, size=shape, dtype=np.uint16) & 0x807F) | 0x3F00
+    k_cache, q = draw(pool, 1, 16, 128), draw(2, 4, 128)
+    dev = DeviceCase(k_cache, k_cache, pt, lens, q)
+    cache = oracle.Cache(k_cache, k_cache, pt, lens, 1)
+    run_and_check(dev, cache, q, np.array([5400, 800], np.int32), 5400, tag="long rows")
+
+
 def test_select_fallback_paths():
     """Threshold bins too large for the LDS candidate list (all keys tied; few distinct
     integer scores over a long context) and an above-bin list larger than its LDS
