@@ -88,8 +88,9 @@ __global__ __launch_bounds__(256) void quest_summary_kernel(const uint16_t *__re
 
 // grid (ceil(max_pages / 256), Hkv * head_blocks, B); 256 threads.  Each wave takes 64
 // pages in 4 batches of 16 (the next batch's summary rows in flight while one is
-// scored); lane group grp of a batch takes pages base + 4 i + grp, i = 0..3, and lane
-// c of the group dims 8c .. 8c + 7.
+// scored; the page-table entries of all 64 arrive first, in one load); lane group grp
+// of a batch takes pages base + 4 i + grp, i = 0..3, and lane c of the group dims
+// 8c .. 8c + 7.
 __global__ __launch_bounds__(256) void quest_bound_kernel(const uint16_t *__restrict__ summary,
                                                           const int32_t *__restrict__ page_table,
                                                           const int32_t *__restrict__ seq_lens,
@@ -109,13 +110,16 @@ __global__ __launch_bounds__(256) void quest_bound_kernel(const uint16_t *__rest
     const int base0 = (int)blockIdx.x * kQuestBoundPages + wave * (kQuestBoundPages / 4);
     if (base0 >= pages) return;                               // wave-uniform
     const int32_t *pt = page_table + (int64_t)b * max_pages;
+    // the wave's 64 page-table entries in one load (lane l: page base0 + l, clamped to
+    // the row), so that the summary loads of every batch go out without another wait
+    const int pt_lane = pt[min(base0 + lane, pages - 1)];
 
     // summary rows of batch j (pages clamped to the row; those past it are not scored)
     auto load_batch = [&](int j, u32x4 (&smin)[4], u32x4 (&smax)[4]) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int p = min(base0 + 16 * j + 4 * i + grp, pages - 1);
-            const int64_t phys = pt[p];
+            const int64_t phys = __shfl(pt_lane, p - base0, 64);
             const uint16_t *row = summary + (phys * num_kv_heads + g) * kQuestSumRows + 8 * c;
             smin[i] = *(const u32x4 *)row;
             smax[i] = *(const u32x4 *)(row + kHeadDim);
