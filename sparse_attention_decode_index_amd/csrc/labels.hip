@@ -63,8 +63,14 @@ __global__ __launch_bounds__(256) void label_build_kernel(const uint16_t *__rest
 // bound) in LDS.  A group of at most four heads takes the four-head form: half the key
 // registers, so four workgroups fit a CU instead of three, and a layer whose
 // workgroups number four per CU runs in one round.
-template <bool kAllKeys, int kHeads>
-__global__ __launch_bounds__(kScoreWaves * 64, kHeads <= 4 ? 4 : 3) void label_score_kernel(
+// kTwo: the workgroup also takes the next 2048 tokens, wave w their slot w.  Those
+// label rows are put in flight as soon as the first slot is scored, so they arrive
+// while the workgroup computes its bound and writes its first records (phases in
+// which it would otherwise read nothing); the second slot's tokens are then scored
+// and filtered against the same bound directly.
+template <bool kAllKeys, int kHeads, bool kTwo>
+__global__ __launch_bounds__(kScoreWaves * 64, kHeads <= 4 ? (kTwo ? 3 : 4) : 3)
+void label_score_kernel(
     const uint16_t *__restrict__ labels, const int32_t *__restrict__ page_table,
     const int32_t *__restrict__ seq_lens, const uint16_t *__restrict__ q, const int32_t *__restrict__ k_per_seq,
     const int32_t *__restrict__ channels, int num_q_heads, int num_kv_heads, int group, int head_blocks,
@@ -78,8 +84,9 @@ __global__ __launch_bounds__(kScoreWaves * 64, kHeads <= 4 ? 4 : 3) void label_s
     const int b = blockIdx.z;
     const int g = blockIdx.y / head_blocks, hb = blockIdx.y - g * head_blocks;
     const int n = seq_lens[b];
-    const int tok0 = blockIdx.x * kScoreTokensPerBlock;
+    const int tok0 = blockIdx.x * kScoreTokensPerBlock * (kTwo ? 2 : 1);
     if (tok0 >= n) return;                                    // whole block exits together
+    const int tok1 = tok0 + kScoreTokensPerBlock;             // the second half (kTwo)
     const int kk = min(min(k_per_seq[b], n), k_max);
     const int heads_here = min(kHeads, group - hb * kHeads);
     const int h0 = g * group + hb * kHeads;
@@ -93,11 +100,12 @@ __global__ __launch_bounds__(kScoreWaves * 64, kHeads <= 4 ? 4 : 3) void label_s
     int32_t chan = 0;
     if (q_lane) chan = channels[g * kLabelDims + qcn];
     const int32_t *pt = page_table + (int64_t)b * max_pages;
-    int32_t phys[kPer];
+    int32_t phys[kPer], phys1[kPer];
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
         const int tl = wave * kWaveTokens + 64 * i + lane;
         phys[i] = pt[(tok0 + min(tl, n_wg - 1)) >> 4];
+        if constexpr (kTwo) phys1[i] = pt[min(tok1 + tl, n - 1) >> 4];   // clamped: always a row of it
     }
     uint32_t qbits = 0;
     if (q_lane) qbits = q[((int64_t)b * num_q_heads + h0 + qh) * kHeadDim + chan];
@@ -127,6 +135,19 @@ __global__ __launch_bounds__(kScoreWaves * 64, kHeads <= 4 ? 4 : 3) void label_s
             }
         }
     }
+    // the second slot's label rows, in flight from here on (every lane loads: a row
+    // past the sequence is replaced by its last row and not scored)
+    u32x4 w1[kPer][2];
+    if constexpr (kTwo) {
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            const int t = min(tok1 + wave * kWaveTokens + 64 * i + lane, n - 1);
+            const int64_t row = ((int64_t)phys1[i] * num_kv_heads + g) * kPage + (t & 15);
+            const u32x4 *lr = (const u32x4 *)(labels + row * kLabelRowElems);
+            w1[i][0] = lr[0];
+            w1[i][1] = lr[1];
+        }
+    }
     if constexpr (kAllKeys) {                                 // every key to the head's key row
 #pragma unroll
         for (int h = 0; h < kHeads; ++h) {
@@ -137,11 +158,21 @@ __global__ __launch_bounds__(kScoreWaves * 64, kHeads <= 4 ? 4 : 3) void label_s
                     const int tl = wave * kWaveTokens + 64 * i + lane;
                     if (tl < n_wg) krow[tl] = key[h][i];
                 }
+                if constexpr (kTwo) {
+                    float qc[kLabelDims];
+#pragma unroll
+                    for (int c = 0; c < kLabelDims; ++c) qc[c] = qc_lds[h][c];
+#pragma unroll
+                    for (int i = 0; i < kPer; ++i) {
+                        const int tl = kScoreTokensPerBlock + wave * kWaveTokens + 64 * i + lane;
+                        if (tok0 + tl < n) krow[tl] = score_key(label_score(qc, w1[i][0], w1[i][1]));
+                    }
+                }
             }
         }
         return;
     } else {
-        __syncthreads();
+        lds_barrier();                                        // codes complete (loads stay in flight)
         // 2. per head (one wave each): the r-th largest code of the workgroup's own keys
         for (int hh = wave; hh < heads_here; hh += kScoreWaves) {
             uint32_t b_lo = 0xFFFFFFFFu;                      // k' = 0 or N: no candidates needed
@@ -177,7 +208,7 @@ __global__ __launch_bounds__(kScoreWaves * 64, kHeads <= 4 ? 4 : 3) void label_s
             }
             if (lane == 0) lo_lds[hh] = b_lo;
         }
-        __syncthreads();
+        lds_barrier();
         // 3. the records: wave w writes slot w of each head straight from its registers;
         //    candidates (keys >= the bound) are placed in token order by ballot; a store
         //    past the record's 192 entries (an overflowed slot) aims past the row and is
@@ -216,6 +247,47 @@ __global__ __launch_bounds__(kScoreWaves * 64, kHeads <= 4 ? 4 : 3) void label_s
                 __builtin_amdgcn_raw_buffer_store_b128(hdr, rsrc, lane == 0 ? rec0 + kCandCap * 4u : kDropOffset, 0, 0);
             }
         }
+        // 4. the second slot (kTwo): scored from the rows in flight and filtered
+        //    against the same bounds, its record written the same way
+        if constexpr (kTwo) {
+            const int s1_tok0 = tok1 + wave * kWaveTokens;
+            if (s1_tok0 >= n) return;                         // wave-uniform
+            const uint32_t rec1 = (uint32_t)(s1_tok0 / kWaveTokens) * kRecWords * 4u;
+#pragma unroll
+            for (int h = 0; h < kHeads; ++h) {
+                if (h < heads_here) {
+                    float qc[kLabelDims];
+#pragma unroll
+                    for (int c = 0; c < kLabelDims; ++c) qc[c] = qc_lds[h][c];
+                    const uint32_t lo = lo_lds[h];
+                    const int64_t row_h = (int64_t)b * num_q_heads + h0 + h;
+                    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+                        cand_rec + row_h * slots * kRecWords, 0, (int)row_bytes, kBufferDword3);
+                    uint32_t cnt = 0, kmax = 0;
+#pragma unroll
+                    for (int i = 0; i < kPer; ++i) {
+                        const bool valid = s1_tok0 + 64 * i + lane < n;
+                        const uint32_t k1 = valid ? score_key(label_score(qc, w1[i][0], w1[i][1])) : 0u;
+                        const bool take = valid && k1 >= lo;
+                        const uint64_t m = __ballot(take);
+                        const uint32_t pos = cnt + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                                             __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+                        const bool put = take && pos < (uint32_t)kCandCap;
+                        __builtin_amdgcn_raw_buffer_store_b32(k1, rsrc, put ? rec1 + 4u * pos : kDropOffset, 0, 0);
+                        __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(64 * i + lane), rsrc,
+                                                              put ? rec1 + (kCandCap + 4) * 4u + 2u * pos : kDropOffset,
+                                                              0, 0);
+                        kmax = max(kmax, take ? k1 : 0u);
+                        cnt += (uint32_t)__popcll(m);
+                    }
+#pragma unroll
+                    for (int o = 32; o > 0; o >>= 1) kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o, 64));
+                    const u32x4 hdr = u32x4{cnt > (uint32_t)kCandCap ? kCandOverflow : cnt, lo, kmax, 0u};
+                    __builtin_amdgcn_raw_buffer_store_b128(hdr, rsrc, lane == 0 ? rec1 + kCandCap * 4u : kDropOffset,
+                                                           0, 0);
+                }
+            }
+        }
     }
 }
 
@@ -245,19 +317,23 @@ hipError_t launch_label_index_topk(const LabelArgs &a, hipStream_t stream)
     uint32_t *keys32 = (uint32_t *)a.ws;
     uint32_t *cand_rec = keys32 + (size_t)a.batch * a.num_q_heads * stride;
     const SelectPlan plan = plan_select(a.k_max, a.n_max, slots);
-    const dim3 grid((a.n_max + kScoreTokensPerBlock - 1) / kScoreTokensPerBlock, a.num_kv_heads * head_blocks,
-                    a.batch);
+    // The four-head form also takes a second slot per wave (measured faster there:
+    // 39.0 -> 37.5 us on the 8 x 32 x 32768 layer); the eight-head form would drop
+    // to two workgroups per CU with it and measured slower.
+    const bool two = heads == 4;
+    const int per_block = (two ? 2 : 1) * kScoreTokensPerBlock;
+    const dim3 grid((a.n_max + per_block - 1) / per_block, a.num_kv_heads * head_blocks, a.batch);
     auto launch_score = [&](auto kernel) {
         hipLaunchKernelGGL(kernel, grid, dim3(kScoreWaves * 64), 0, stream, (const uint16_t *)a.labels,
                            a.page_table, a.seq_lens, (const uint16_t *)a.q, a.k_per_seq, a.channels, a.num_q_heads,
                            a.num_kv_heads, group, head_blocks, a.max_pages, a.k_max, cand_rec, slots, keys32, stride);
     };
-    if (heads == 4) {
-        if (plan.all_keys) launch_score(label_score_kernel<true, 4>);
-        else launch_score(label_score_kernel<false, 4>);
+    if (two) {
+        if (plan.all_keys) launch_score(label_score_kernel<true, 4, true>);
+        else launch_score(label_score_kernel<false, 4, true>);
     } else {
-        if (plan.all_keys) launch_score(label_score_kernel<true, kHeadBlock>);
-        else launch_score(label_score_kernel<false, kHeadBlock>);
+        if (plan.all_keys) launch_score(label_score_kernel<true, kHeadBlock, false>);
+        else launch_score(label_score_kernel<false, kHeadBlock, false>);
     }
     SelectArgs s{(const uint16_t *)a.k_cache, a.page_table, a.seq_lens, a.k_per_seq, (const uint16_t *)a.q,
                  cand_rec, slots, plan.cap, plan.all_keys ? 1 : 0, keys32, stride, a.num_q_heads, a.num_kv_heads,
