@@ -113,3 +113,75 @@ def test_sampled_full_size(cfg, sample):
     assert np.all(np.abs(gw[sub] - ow) <= 2.0 ** -23 * ow)
     cache, q = _sub_cache(wl, sub), wl.q[sub]
     check_close(out[sub], oracle.attend_sampled(cache, q, idx[sub], gs[sub], ow), what=f"C{cfg} attend_sampled")
+
+
+def test_next_rows_graph_replay_matches_eager():
+    """The label step (current-page label update, label index, attend), the Quest step
+    (current-page summaries, page selection, attend) and the stochastic step (index,
+    draws, two-list attend) captured in one HIP graph and replayed several times, with
+    eager work and synchronisation between replays: every replay reproduces the eager
+    results bit for bit."""
+    wl = synth.config(2, n=5000, batch=2)
+    dev = DeviceCase.of_workload(wl)
+    B, hq = wl.batch, wl.num_q_heads
+    k = wl.k_per_seq()
+    k_max = int(k.max())
+    kps = i32_tensor(k)
+    ch = i32_tensor(_calibrated_channels(wl))
+    labels = sdi.label_build(dev.kv, ch)
+    summary = sdi.quest_summarize(dev.kv)
+    m = -(-k_max // 16)
+    mps, tps = i32_tensor(np.full(B, m, np.int32)), i32_tensor(np.full(B, 16 * m, np.int32))
+    kd, sv = i32_tensor((k + 1) // 2), i32_tensor(k // 2)
+    kd_max, s_max = (k_max + 1) // 2, max(1, k_max // 2)
+    rng = np.random.default_rng(67)
+    draws = torch.from_numpy(rng.integers(0, 2 ** 32, size=(B, hq, s_max), dtype=np.uint64)
+                             .astype(np.uint32).view(np.int32)).cuda()
+    cuda = dict(device="cuda")
+    lidx = torch.empty((B, hq, k_max), dtype=torch.int32, **cuda)
+    qidx = torch.empty((B, hq, 16 * m), dtype=torch.int32, **cuda)
+    kidx = torch.empty((B, hq, kd_max), dtype=torch.int32, **cuda)
+    smp = torch.empty((B, hq, s_max), dtype=torch.int32, **cuda)
+    wt = torch.empty((B, hq), dtype=torch.float32, **cuda)
+    outs = [torch.empty((B, hq, 128), dtype=torch.float32, **cuda) for _ in range(3)]
+    ws_i = torch.empty(sdi.index_topk_workspace_bytes(dev.kv, hq, k_max), dtype=torch.uint8, **cuda)
+    ws_a = torch.empty(max(1, sdi.attend_workspace_bytes(dev.kv, hq, 16 * m)), dtype=torch.uint8, **cuda)
+    ws_q = torch.empty(max(1, sdi.load_library().sparse_decode_quest_select_workspace(
+        __import__("ctypes").byref(dev.kv.struct()), hq, m)), dtype=torch.uint8, **cuda)
+    ws_s = torch.empty(max(1, sdi.attend_sampled_workspace_bytes(dev.kv, hq, kd_max, s_max)), dtype=torch.uint8,
+                       **cuda)
+
+    def step():
+        st = torch.cuda.current_stream()
+        sdi.label_build(dev.kv, ch, labels, current_pages_only=True, stream=st)
+        sdi.label_index_topk(dev.kv, dev.q, labels, ch, kps, k_max, idx_out=lidx, workspace=ws_i, stream=st)
+        sdi.attend(dev.kv, dev.q, lidx, kps, out=outs[0], workspace=ws_a, stream=st)
+        sdi.quest_summarize(dev.kv, summary, current_pages_only=True, stream=st)
+        sdi.quest_select(dev.kv, dev.q, summary, mps, m, idx_out=qidx, workspace=ws_q, stream=st)
+        sdi.attend(dev.kv, dev.q, qidx, tps, out=outs[1], workspace=ws_a, stream=st)
+        sdi.index_topk(dev.kv, dev.q, kd, kd_max, idx_out=kidx, workspace=ws_i, stream=st)
+        sdi.sample_residual(dev.kv, kidx, kd, draws, sv, sample_out=smp, weight_out=wt, stream=st)
+        sdi.attend_sampled(dev.kv, dev.q, kidx, kd, smp, wt, sv, out=outs[2], workspace=ws_s, stream=st)
+
+    results = lambda: [t.clone() for t in (lidx, qidx, kidx, smp, wt, *outs)]
+    step()
+    torch.cuda.synchronize()
+    want = results()
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        step()
+    for rep in range(4):
+        for t in (lidx, qidx, kidx, smp):
+            t.fill_(-7)
+        for t in (wt, *outs):
+            t.fill_(float("nan"))
+        for t in (ws_i, ws_a, ws_q, ws_s):
+            t.fill_(0xAB)                                    # stale scratch must not matter
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        _say(f"[graph] replay {rep}")
+        got = results()
+        for j, (a, b) in enumerate(zip(got, want)):
+            assert torch.equal(a, b), (rep, j)
