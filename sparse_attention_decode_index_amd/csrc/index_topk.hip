@@ -795,14 +795,18 @@ SelectPlan plan_select(int k_max, int n_max, int slots)
 hipError_t launch_select(const SelectArgs &s, const SelectPlan &p, int batch, hipStream_t stream)
 {
     if (p.dyn > 64 * 1024) {
-        // raise the kernel's dynamic-LDS limit to the budget once (a function attribute,
-        // not a stream operation)
-        static std::atomic<bool> raised{false};
-        if (!raised.load(std::memory_order_acquire)) {
-            const hipError_t e = hipFuncSetAttribute((const void *)select_kernel,
-                                                     hipFuncAttributeMaxDynamicSharedMemorySize, kSelDynMax);
+        // raise the kernel's dynamic-LDS limit to the budget once per device (a function
+        // attribute, not a stream operation)
+        static std::atomic<uint64_t> raised{0};
+        int dev = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e != hipSuccess) return e;
+        const uint64_t bit = dev < 64 ? (uint64_t)1 << dev : 0;
+        if (bit == 0 || !(raised.load(std::memory_order_acquire) & bit)) {
+            e = hipFuncSetAttribute((const void *)select_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                    kSelDynMax);
             if (e != hipSuccess) return e;
-            raised.store(true, std::memory_order_release);
+            raised.fetch_or(bit, std::memory_order_acq_rel);
         }
     }
     hipLaunchKernelGGL(select_kernel, dim3(s.num_q_heads, batch), dim3(kSelThreads), p.dyn, stream, s);
