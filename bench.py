@@ -41,7 +41,8 @@ def parse_args():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
-    ap.add_argument("--cold", action="store_true", help="also time each launch group after a 1 GiB cache flush")
+    ap.add_argument("--no-cold", action="store_true",
+                    help="skip timing each launch group after a 1 GiB cache flush (eager launches)")
     ap.add_argument("--mode", choices=("graph", "eager"), default="graph",
                     help="replay captured HIP graphs (default) or launch eagerly from Python")
     ap.add_argument("--quest", action="store_true",
@@ -117,7 +118,16 @@ def cpu_baseline(wl, target_s):
         total += run(nb)
         reps += 1
     per_step = total / reps * wl.batch / nb
+    cpu_model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu_model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     return {"value": 1.0 / per_step, "unit": "decode steps/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "nproc": os.cpu_count(), "cpu_model": cpu_model,
             "sample": f"{reps} x the oracle's decode step (fp64 scores, exact top-k, attend) on {nb} of "
                       f"{wl.batch} sequences ({total:.1f} s), scaled to the whole batch"}
 
@@ -510,7 +520,9 @@ def main():
                               dense_s)
 
     cold = {}
-    if args.cold:
+    if not args.no_cold:
+        # the 256 MB Infinity Cache and the L2s flushed by writing 1 GiB before each
+        # step; eager launches, so the figures include the host's launch gaps
         flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         ci, ca = [], []
         for s in range(10):
@@ -521,6 +533,9 @@ def main():
             ci.append(e[0].elapsed_time(e[1]) * 1e-3)
             ca.append(e[1].elapsed_time(e[2]) * 1e-3)
         cold = {"index_us_cold": float(np.median(ci) * 1e6), "attend_us_cold": float(np.median(ca) * 1e6)}
+        b_i, b_a, _ = algorithmic_bytes(wl.seq_lens, wl.k_per_seq(), B, hq, hkv)
+        cold["index_pct_of_peak_cold"] = 100 * b_i / (cold["index_us_cold"] * 1e-6) / PEAK_HBM_BPS
+        cold["attend_pct_of_peak_cold"] = 100 * b_a / (cold["attend_us_cold"] * 1e-6) / PEAK_HBM_BPS
         del flush
 
     if args.calibration_copy_mib > 0:
