@@ -520,7 +520,7 @@ def main():
                               dense_s)
 
     cold = {}
-    if not args.no_cold:
+    if not args.no_cold and args.mode == "graph":
         # the 256 MB Infinity Cache and the L2s flushed by writing 1 GiB before each
         # step; eager launches, so the figures include the host's launch gaps
         flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
