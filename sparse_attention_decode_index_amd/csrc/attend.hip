@@ -61,37 +61,46 @@ __global__ __launch_bounds__(MAXW * 64) void attend_kernel(
     const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int64_t bh = (int64_t)b * num_q_heads + h;
     const int g = h / group;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int grp = lane >> 4, sub = lane & 15;
+    const int i0 = split * waves * kAttPerWave;
+    const int i = i0 + wave * kAttPerWave + lane;   // the entry this lane resolves
+    // The lane's index entry and the q row are loaded together with the row's length
+    // (the entry is clamped into the row and discarded below when i >= k'), so the
+    // index load does not wait for k_per_seq.
+    // Absent per-sequence counts read seq_lens in their place (value unused), so no load
+    // sits behind a branch on a null pointer.
     const int n = seq_lens[b];
-    int kk = k_per_seq ? min(k_per_seq[b], k_max) : k_max;
+    const int k_raw = (k_per_seq ? k_per_seq : seq_lens)[b];
+    const int s_raw = SAMPLED ? (s_per_seq ? s_per_seq : seq_lens)[b] : 0;
+    const int j_top = idx[bh * k_max + min(i, k_max - 1)];
+    const u32x4 qw = *(const u32x4 *)(q + bh * kHeadDim + sub * 8);
+    int kk = k_per_seq ? min(k_raw, k_max) : k_max;
     if (kk < 0) kk = 0;
     int len = kk;                            // entries of this row
-    if (SAMPLED) len += max(s_per_seq ? min(s_per_seq[b], s_max) : s_max, 0);
-    const int i0 = split * waves * kAttPerWave;
-    if (i0 >= len) {                         // nothing listed in this chunk
+    if (SAMPLED) len += max(s_per_seq ? min(s_raw, s_max) : s_max, 0);
+    // A chunk past the row's entries exits.  The one-workgroup form (split 0 only) has no
+    // such branch: with nothing listed every row is masked and it writes zeros below, and
+    // without the branch the index and q loads above are issued before the counts arrive.
+    if (MAXW != kAttMaxWaves && i0 >= len) {
         if (splits == 1)
             for (int t = threadIdx.x; t < kHeadDim; t += blockDim.x) out[bh * kHeadDim + t] = 0.f;
         return;                              // (chunks past k are never merged)
     }
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int grp = lane >> 4, sub = lane & 15;
 
     float qf[8];
-    {
-        const u32x4 w = *(const u32x4 *)(q + bh * kHeadDim + sub * 8);
-        unpack8(w, qf);
+    unpack8(qw, qf);
 #pragma unroll
-        for (int d = 0; d < 8; ++d) qf[d] *= scale_log2;
-    }
+    for (int d = 0; d < 8; ++d) qf[d] *= scale_log2;
 
     // Each lane resolves one index of the wave's 64 to a cache row number (-1 = skip);
     // in two-list mode also to its base-2 log weight (0 for top-k entries).
     int my_row = -1;
     float my_lw = 0.f;
     {
-        const int i = i0 + wave * kAttPerWave + lane;
         int j = -1;
         if (i < kk) {
-            j = idx[bh * k_max + i];
+            j = j_top;
         } else if (SAMPLED && i < len) {
             j = sample[bh * s_max + (i - kk)];
             my_lw = log2f(sample_weight[bh]);
