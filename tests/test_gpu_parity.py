@@ -226,6 +226,25 @@ def test_attend_accepts_any_index_list():
     assert np.all(gpu[0, 0] == 0)
 
 
+@pytest.mark.parametrize("k_max", [700, 1300], ids=["one-workgroup", "chunked"])
+def test_attend_counts_cut_the_list(k_max):
+    """k_per_seq limits the row to its first k_b entries even where the list holds more;
+    k_b = 0 gives 0 and k_b > k_max is clamped to k_max."""
+    rng = np.random.default_rng(19)
+    case = random_case(rng, batch=3, hq=4, hkv=2, lens=[1500, 3000, 2000])
+    dev = DeviceCase.of_tiny(case)
+    cache = oracle.Cache(case.k_cache, case.v_cache, case.page_table, case.lens)
+    idx = np.stack([np.stack([np.sort(rng.choice(case.lens[b], size=k_max, replace=False)) for _ in range(4)])
+                    for b in range(3)]).astype(np.int32)
+    kps = np.array([0, 37, k_max + 500], np.int32)
+    gpu = dev.attend(idx, kps)
+    cut = idx.copy()
+    for b in range(3):
+        cut[b, :, min(kps[b], k_max):] = -1
+    assert np.all(gpu[0] == 0)
+    check_close(gpu[1:], oracle.attend(cache, case.q, cut)[1:], what="counts")
+
+
 def test_layout_invariance_and_determinism():
     rng = np.random.default_rng(10)
     base = random_case(rng, batch=3, hq=8, hkv=2, lens=[2000, 333, 4100], layout="contiguous")
