@@ -271,11 +271,14 @@ def test_workspace_too_small_is_rejected():
 
 # ------------------------------------------------------------------------ full size, sampled
 
-@pytest.mark.parametrize("cfg,sample", [(2, [0, 5]), (3, [2])], ids=["C2-full", "C3-full"])
-def test_full_size_sampled(cfg, sample):
+@pytest.mark.parametrize("cfg,ratio,sample", [(2, None, [0, 5]), (3, None, [2]), (4, 20, [7]), (5, None, [4, 17])],
+                         ids=["C2-full", "C3-full", "C4-full-k=N/20", "C5-full"])
+def test_full_size_sampled(cfg, ratio, sample):
     """The full decode layer in the benchmark's launch configuration; the oracle checks
-    every head of the sampled sequences, and properties are checked for every row."""
-    wl = synth.config(cfg)
+    every head of the sampled sequences, and properties are checked for every row.  The
+    sweep runs at its most crowded candidate-path budget (k = N/20); the agentic batch
+    at its first step (its ragged rows, fragmented pages and per-sequence k)."""
+    wl = synth.config(cfg, ratio=ratio)
     dev = DeviceCase.of_workload(wl)
     kps = wl.k_per_seq()
     k_max = wl.k_max()
