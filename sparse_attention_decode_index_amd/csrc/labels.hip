@@ -56,13 +56,13 @@ __global__ __launch_bounds__(256) void label_build_kernel(const uint16_t *__rest
         uint2{v[0] | (v[1] << 16), v[2] | (v[3] << 16)};
 }
 
-// grid (ceil(n_max / 2048), Hkv * head_blocks, B); 256 threads; up to kHeads q heads
-// per workgroup.  Wave w owns the workgroup's slot w (tokens 512 w .. 512 w + 511),
-// lane l its tokens 512 w + 64 i + l, i = 0..7: it scores them, keeps their keys in
-// registers for the records, and shares only their 16-bit codes (for the workgroup's
-// bound) in LDS.  A group of at most four heads takes the four-head form: half the key
-// registers, so four workgroups fit a CU instead of three, and a layer whose
-// workgroups number four per CU runs in one round.
+// grid (ceil(n_max / (2048 (kTwo ? 2 : 1))), Hkv * head_blocks, B); 256 threads; up to
+// kHeads q heads per workgroup.  Wave w owns the workgroup's slot w (tokens 512 w ..
+// 512 w + 511), lane l its tokens 512 w + 64 i + l, i = 0..7: it scores them, keeps
+// their keys in registers for the records, and shares only their 16-bit codes (for the
+// workgroup's bound) in LDS.  A group of at most four heads takes the four-head form:
+// half the key registers, which leaves room for a second slot's label rows (kTwo) at
+// three workgroups per CU (four without them).
 // kTwo: the workgroup also takes the next 2048 tokens, wave w their slot w.  Those
 // label rows are put in flight as soon as the first slot is scored, so they arrive
 // while the workgroup computes its bound and writes its first records (phases in
