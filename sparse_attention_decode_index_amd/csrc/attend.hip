@@ -65,11 +65,10 @@ __global__ __launch_bounds__(MAXW * 64) void attend_kernel(
     const int grp = lane >> 4, sub = lane & 15;
     const int i0 = split * waves * kAttPerWave;
     const int i = i0 + wave * kAttPerWave + lane;   // the entry this lane resolves
-    // The lane's index entry and the q row are loaded together with the row's length
-    // (the entry is clamped into the row and discarded below when i >= k'), so the
-    // index load does not wait for k_per_seq.
-    // Absent per-sequence counts read seq_lens in their place (value unused), so no load
-    // sits behind a branch on a null pointer.
+    // The lane's index entry and the q row load together with the row's counts (the
+    // entry is clamped into the row and discarded below when i >= k'), so the index
+    // load does not wait for k_per_seq.  Absent per-sequence counts read seq_lens in
+    // their place (value unused): no load sits behind a branch on a null pointer.
     const int n = seq_lens[b];
     const int k_raw = (k_per_seq ? k_per_seq : seq_lens)[b];
     const int s_raw = SAMPLED ? (s_per_seq ? s_per_seq : seq_lens)[b] : 0;
