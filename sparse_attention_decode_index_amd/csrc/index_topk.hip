@@ -523,6 +523,7 @@ struct LdsCandidates {
 // Generic path for one head: re-score every token to its full 32-bit key in the
 // workspace row (from the K rows, or from the label rows for the lightweight
 // indexer), then radix-select over the keys.  Called by the whole workgroup.
+template <int kThreads>
 __device__ __forceinline__ void select_rescore_generic(const SelectArgs &a, int64_t bh, int b, int h, int n, int kk,
                                                        uint32_t *hist, uint32_t *scratch, uint32_t *res,
                                                        int32_t *__restrict__ out)
@@ -539,19 +540,19 @@ __device__ __forceinline__ void select_rescore_generic(const SelectArgs &a, int6
         float qc[kLabelDims];
 #pragma unroll
         for (int i = 0; i < kLabelDims; ++i) qc[i] = __uint_as_float((uint32_t)qrow[ch[i]] << 16);
-        for (int tok = threadIdx.x; tok < n; tok += kSelThreads) {
+        for (int tok = threadIdx.x; tok < n; tok += kThreads) {
             const int64_t row = ((int64_t)pt[tok >> 4] * a.num_kv_heads + g) * kPage + (tok & 15);
             const u32x4 *lr = (const u32x4 *)(a.labels + row * kLabelDims);
             krow[tok] = score_key(label_score(qc, lr[0], lr[1]));
         }
         __threadfence_block();
         __syncthreads();
-        radix_select(RowKeys{krow}, n, kk, a.k_max, 0u, 32, 0u, hist, scratch, res, out);
+        radix_select<kThreads>(RowKeys{krow}, n, kk, a.k_max, 0u, 32, 0u, hist, scratch, res, out);
         return;
     }
     bf16x8 qb[4];
     load_q_operand(qb, a.q, (int64_t)b * a.num_q_heads + g * a.group + hb * kHeadBlock, heads_here, col, quad);
-    for (int t0 = wave * 16; t0 < n; t0 += kSelWaves * 16) {
+    for (int t0 = wave * 16; t0 < n; t0 += (kThreads / 64) * 16) {
         const int tok = t0 + col;
         const int row = tok < n ? (pt[tok >> 4] * a.num_kv_heads + g) * kPage + (tok & 15) : -1;
         const f32x4 acc = rescore16(a.kc, row, qb, quad);
@@ -563,16 +564,18 @@ __device__ __forceinline__ void select_rescore_generic(const SelectArgs &a, int6
     }
     __threadfence_block();
     __syncthreads();
-    radix_select(RowKeys{krow}, n, kk, a.k_max, 0u, 32, 0u, hist, scratch, res, out);
+    radix_select<kThreads>(RowKeys{krow}, n, kk, a.k_max, 0u, 32, 0u, hist, scratch, res, out);
 }
 
-// grid (num_q_heads, batch); kSelThreads threads; dynamic LDS holds the candidates.
-__global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a)
+// grid (num_q_heads, batch); kThreads threads (512, or 1024 when the rows are fewer
+// than the CUs); dynamic LDS holds the candidates.
+template <int kThreads>
+__global__ __launch_bounds__(kThreads) void select_kernel(SelectArgs a)
 {
     // keys[cap] | first[slots + 1] | blk[cap / 64] | positions (16-bit) [cap]
     extern __shared__ __attribute__((aligned(16))) uint32_t dyn_lds[];
     __shared__ __attribute__((aligned(16))) uint32_t hist[kHistBins];
-    __shared__ uint32_t scratch[kSelWaves + 2];
+    __shared__ uint32_t scratch[kThreads / 64 + 2];
     __shared__ uint32_t res[8];
     __shared__ uint32_t blist[64];                            // keys of the threshold bin
 
@@ -587,11 +590,11 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a)
     if (kk < 0) kk = 0;
     int32_t *out = a.idx_out + bh * a.k_max;
     if (kk == n || kk == 0) {                                 // everything, or nothing
-        for (int i = threadIdx.x; i < a.k_max; i += kSelThreads) out[i] = i < kk ? i : -1;
+        for (int i = threadIdx.x; i < a.k_max; i += kThreads) out[i] = i < kk ? i : -1;
         return;
     }
     if (a.all_keys) {
-        radix_select(RowKeys{a.keys32 + bh * a.stride}, n, kk, a.k_max, 0u, 32, 0u, hist, scratch, res, out);
+        radix_select<kThreads>(RowKeys{a.keys32 + bh * a.stride}, n, kk, a.k_max, 0u, 32, 0u, hist, scratch, res, out);
         return;
     }
     bool generic = a.cap == 0;
@@ -605,8 +608,8 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a)
         //    overflowed slot sends the row to the generic path.
         int bad = 0;
         uint32_t lo_max = 0u, hi_max = 0u;
-        for (int i = threadIdx.x; i < kHistBins; i += kSelThreads) hist[i] = 0u;
-        for (int base = 0; base < a.slots; base += kSelThreads) {
+        for (int i = threadIdx.x; i < kHistBins; i += kThreads) hist[i] = 0u;
+        for (int base = 0; base < a.slots; base += kThreads) {
             // loaded for every allocated slot (no wait for seq_lens), used below nslots
             const int i = base + (int)threadIdx.x;
             const bool in_ws = i < a.slots;
@@ -623,7 +626,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a)
             c = ovf ? 0u : c;
             bad |= __syncthreads_or(ovf ? 1 : 0);
             uint32_t tot;
-            const uint32_t p0 = total + block_exclusive_scan<kSelThreads>(c, scratch, tot);
+            const uint32_t p0 = total + block_exclusive_scan<kThreads>(c, scratch, tot);
             if (in_ws) first[i] = p0;
             for (uint32_t v = (p0 + 63u) & ~63u; v < p0 + c && v < (uint32_t)a.cap; v += 64u) blk[v >> 6] = (uint32_t)i;
             total += tot;
@@ -642,7 +645,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a)
         __syncthreads();                                      // map, bounds and cleared histogram complete
     }
     if (generic) {
-        select_rescore_generic(a, bh, b, h, n, kk, hist, scratch, res, out);
+        select_rescore_generic<kThreads>(a, bh, b, h, n, kk, hist, scratch, res, out);
         return;
     }
     // 2. gather the candidates into LDS in token order: thread t takes list positions
@@ -658,12 +661,12 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a)
     const int w0 = min(kHistBits, bits), sh0 = bits - w0;
     const uint32_t mask0 = (1u << w0) - 1u;
     uint32_t eligible = 0;                                    // keys >= lo this thread gathered
-    for (uint32_t v0 = 0; v0 < total; v0 += kSelThreads * kGatherUnroll) {
+    for (uint32_t v0 = 0; v0 < total; v0 += kThreads * kGatherUnroll) {
         uint32_t key[kGatherUnroll];
         uint16_t ps[kGatherUnroll];
 #pragma unroll
         for (int u = 0; u < kGatherUnroll; ++u) {
-            const uint32_t v = v0 + u * kSelThreads + threadIdx.x;
+            const uint32_t v = v0 + u * kThreads + threadIdx.x;
             if (v < total) {
                 const int i = slot_of_position(first, blk, v);
                 const uint32_t *rec = rec_row + (int64_t)i * kRecWords;
@@ -674,7 +677,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a)
         }
 #pragma unroll
         for (int u = 0; u < kGatherUnroll; ++u) {
-            const uint32_t v = v0 + u * kSelThreads + threadIdx.x;
+            const uint32_t v = v0 + u * kThreads + threadIdx.x;
             if (v < total) {
                 ckey[v] = key[u];
                 cpos[v] = ps[u];
@@ -691,7 +694,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a)
     __syncthreads();
     if (res[4] < (uint32_t)kk) {                              // fewer than k keys reach every bound
         __syncthreads();
-        select_rescore_generic(a, bh, b, h, n, kk, hist, scratch, res, out);
+        select_rescore_generic<kThreads>(a, bh, b, h, n, kk, hist, scratch, res, out);
         return;
     }
     // 3. the k-th key T and r, the number of keys equal to T to take (the first ones):
@@ -708,7 +711,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a)
             T = floor0;
             r = 0xFFFFFFFFu;
         } else {
-            for (uint32_t v = threadIdx.x; v < total; v += kSelThreads) {
+            for (uint32_t v = threadIdx.x; v < total; v += kThreads) {
                 const uint32_t key = ckey[v];
                 if (key >= lo && ((key - lo) >> sh0) == b0) {
                     const uint32_t at = atomicAdd(&res[2], 1u);
@@ -719,8 +722,8 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a)
             const uint32_t m = res[2];
             if (m > 64u) {                                    // a crowded bin: full radix passes
                 __syncthreads();
-                if (!radix_select(cands, (int)total, kk, a.k_max, lo, bits, lo_max, hist, scratch, res, out))
-                    select_rescore_generic(a, bh, b, h, n, kk, hist, scratch, res, out);
+                if (!radix_select<kThreads>(cands, (int)total, kk, a.k_max, lo, bits, lo_max, hist, scratch, res, out))
+                    select_rescore_generic<kThreads>(a, bh, b, h, n, kk, hist, scratch, res, out);
                 return;
             }
             if (threadIdx.x < 64) {                           // need0-th largest of the bin, by rank
@@ -743,10 +746,10 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(SelectArgs a)
     }
     if (T < lo_max) {                                         // some workgroup's bound lies above T
         __syncthreads();
-        select_rescore_generic(a, bh, b, h, n, kk, hist, scratch, res, out);
+        select_rescore_generic<kThreads>(a, bh, b, h, n, kk, hist, scratch, res, out);
         return;
     }
-    compact_selected(cands, (int)total, kk, a.k_max, T, r, scratch, out);
+    compact_selected<kThreads>(cands, (int)total, kk, a.k_max, T, r, scratch, out);
 }
 
 // ---- host side ---------------------------------------------------------------------------
@@ -792,7 +795,8 @@ SelectPlan plan_select(int k_max, int n_max, int slots)
     return SelectPlan{cap, dyn, all_keys};
 }
 
-hipError_t launch_select(const SelectArgs &s, const SelectPlan &p, int batch, hipStream_t stream)
+template <int kThreads>
+static hipError_t launch_select_with(const SelectArgs &s, const SelectPlan &p, int batch, hipStream_t stream)
 {
     if (p.dyn > 64 * 1024) {
         // raise the kernel's dynamic-LDS limit to the budget once per device (a function
@@ -803,14 +807,25 @@ hipError_t launch_select(const SelectArgs &s, const SelectPlan &p, int batch, hi
         if (e != hipSuccess) return e;
         const uint64_t bit = dev < 64 ? (uint64_t)1 << dev : 0;
         if (bit == 0 || !(raised.load(std::memory_order_acquire) & bit)) {
-            e = hipFuncSetAttribute((const void *)select_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+            e = hipFuncSetAttribute((const void *)select_kernel<kThreads>, hipFuncAttributeMaxDynamicSharedMemorySize,
                                     kSelDynMax);
             if (e != hipSuccess) return e;
             raised.fetch_or(bit, std::memory_order_acq_rel);
         }
     }
-    hipLaunchKernelGGL(select_kernel, dim3(s.num_q_heads, batch), dim3(kSelThreads), p.dyn, stream, s);
+    hipLaunchKernelGGL(select_kernel<kThreads>, dim3(s.num_q_heads, batch), dim3(kThreads), p.dyn, stream, s);
     return hipGetLastError();
+}
+
+hipError_t launch_select(const SelectArgs &s, const SelectPlan &p, int batch, hipStream_t stream)
+{
+    // Fewer rows than CUs leave CUs idle: long rows then take twice the threads (the
+    // 160-row long-retrieval batch measured 3.6 us faster; with a row or more per CU,
+    // or short rows, 512 threads measured faster).
+    const bool few_rows = (int64_t)s.num_q_heads * batch < kCUs;
+    const bool long_rows = s.cap >= 4096 || (s.all_keys && s.stride >= 65536);
+    if (few_rows && long_rows) return launch_select_with<1024>(s, p, batch, stream);
+    return launch_select_with<kSelThreads>(s, p, batch, stream);
 }
 
 hipError_t launch_index_topk(const IndexArgs &a, hipStream_t stream)

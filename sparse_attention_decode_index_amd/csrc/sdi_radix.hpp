@@ -92,7 +92,7 @@ struct RowKeys {
     }
 };
 
-template <class Src>
+template <int kThreads = kSelThreads, class Src>
 __device__ __forceinline__ void compact_selected(const Src &src, int n, int kk, int k_max, uint32_t T, uint32_t r,
                                                  uint32_t *scratch, int32_t *__restrict__ out);
 
@@ -103,7 +103,7 @@ __device__ __forceinline__ void compact_selected(const Src &src, int n, int kk, 
 // tokens ascending and pads the row with -1.  Returns false, writing nothing, if
 // T < min_t.  With first_hist_ready the caller has already counted the first digit
 // into hist (and zeroed res[0..1]).
-template <class Src>
+template <int kThreads = kSelThreads, class Src>
 __device__ __forceinline__ bool radix_select(const Src &src, int n, int kk, int k_max, uint32_t base, int bits,
                                              uint32_t min_t, uint32_t *hist, uint32_t *scratch, uint32_t *res,
                                              int32_t *__restrict__ out, bool first_hist_ready = false)
@@ -115,10 +115,10 @@ __device__ __forceinline__ bool radix_select(const Src &src, int n, int kk, int 
     while (hi > 0) {
         const int w = min(kHistBits, hi), lo = hi - w, nb = max(64, 1 << w);
         if (!ready) {
-            for (int i = threadIdx.x; i < nb; i += kSelThreads) hist[i] = 0u;
+            for (int i = threadIdx.x; i < nb; i += kThreads) hist[i] = 0u;
             if (threadIdx.x == 0) { res[0] = 0u; res[1] = 0u; }
             __syncthreads();
-            for (int i0 = 0; i0 < n; i0 += kSelTile) {
+            for (int i0 = 0; i0 < n; i0 += kThreads * kSelPerThread) {
                 uint32_t v[8];
                 const int cnt = src.load8(i0 + threadIdx.x * kSelPerThread, n, v);
 #pragma unroll
@@ -140,18 +140,19 @@ __device__ __forceinline__ bool radix_select(const Src &src, int n, int kk, int 
     prefix += base;
     const uint32_t T = prefix, r = need;                     // take keys > T and the first r keys == T
     if (T < min_t) return false;
-    compact_selected(src, n, kk, k_max, T, r, scratch, out);
+    compact_selected<kThreads>(src, n, kk, k_max, T, r, scratch, out);
     return true;
 }
 
 // Ordered compaction: writes, in token order, the keys > T and the first r keys == T
 // (at most kk tokens), then pads the row to k_max with -1.
-template <class Src>
+template <int kThreads, class Src>
 __device__ __forceinline__ void compact_selected(const Src &src, int n, int kk, int k_max, uint32_t T, uint32_t r,
                                                  uint32_t *scratch, int32_t *__restrict__ out)
 {
+    constexpr int kTile = kThreads * kSelPerThread;
     uint32_t run_sel = 0, run_eq = 0;
-    for (int base = 0; base < n; base += kSelTile) {
+    for (int base = 0; base < n; base += kTile) {
         uint32_t v[8];
         const int start = base + threadIdx.x * kSelPerThread;
         const int cnt = src.load8(start, n, v);
@@ -164,7 +165,7 @@ __device__ __forceinline__ void compact_selected(const Src &src, int n, int kk, 
         int32_t tk[8];
         if (gt + eq > 0u) src.tokens8(start, cnt, tk);        // loads in flight before the scan
         uint32_t tot;
-        const uint32_t pre = block_exclusive_scan<kSelThreads>((eq << 16) | gt, scratch, tot);
+        const uint32_t pre = block_exclusive_scan<kThreads>((eq << 16) | gt, scratch, tot);
         const uint32_t eq_left = r > run_eq ? r - run_eq : 0u;
         uint32_t pos = run_sel + (pre & 0xFFFFu) + min(pre >> 16, eq_left);
         uint32_t eq_rank = run_eq + (pre >> 16);
@@ -182,7 +183,7 @@ __device__ __forceinline__ void compact_selected(const Src &src, int n, int kk, 
         run_sel += (tot & 0xFFFFu) + min(tot >> 16, eq_left);
         run_eq += tot >> 16;
     }
-    for (int i = (int)run_sel + threadIdx.x; i < k_max; i += kSelThreads) out[i] = -1;
+    for (int i = (int)run_sel + threadIdx.x; i < k_max; i += kThreads) out[i] = -1;
 }
 
 }  // namespace sdi
