@@ -23,6 +23,7 @@
 //     selection (lower page first on equal keys), then the selected pages'
 //     tokens j < N_b ascending, -1 elsewhere, ready for the gather-attend.
 #include "sdi_device.hpp"
+#include "sdi_index.hpp"
 #include "sdi_launch.hpp"
 #include "sdi_radix.hpp"
 
@@ -167,8 +168,10 @@ __global__ __launch_bounds__(256) void quest_bound_kernel(const uint16_t *__rest
     score_batch(3, bmin, bmax);
 }
 
-// grid (Hq, B); kSelThreads threads.
-__global__ __launch_bounds__(kSelThreads) void quest_select_kernel(const uint32_t *__restrict__ keys,
+// grid (Hq, B); kThreads threads (512, or 1024 when the rows are fewer than the CUs and
+// long).
+template <int kThreads>
+__global__ __launch_bounds__(kThreads) void quest_select_kernel(const uint32_t *__restrict__ keys,
                                                                    int64_t key_stride,
                                                                    const int32_t *__restrict__ seq_lens,
                                                                    const int32_t *__restrict__ m_per_seq,
@@ -177,7 +180,7 @@ __global__ __launch_bounds__(kSelThreads) void quest_select_kernel(const uint32_
                                                                    int32_t *__restrict__ idx_out)
 {
     __shared__ __attribute__((aligned(16))) uint32_t hist[kHistBins];
-    __shared__ uint32_t scratch[kSelWaves + 2];
+    __shared__ uint32_t scratch[kThreads / 64 + 2];
     __shared__ uint32_t res[8];
     const int h = blockIdx.x, b = blockIdx.y;
     const int64_t bh = (int64_t)b * num_q_heads + h;
@@ -189,12 +192,12 @@ __global__ __launch_bounds__(kSelThreads) void quest_select_kernel(const uint32_
     if (!all && m > 0) {
         if (threadIdx.x < 8) res[threadIdx.x] = 0u;
         __syncthreads();
-        radix_select(RowKeys{keys + bh * key_stride}, pages, m, m_max, 0u, 32, 0u, hist, scratch, res, prow);
+        radix_select<kThreads>(RowKeys{keys + bh * key_stride}, pages, m, m_max, 0u, 32, 0u, hist, scratch, res, prow);
         __threadfence_block();
         __syncthreads();                                      // the page list is written
     }
     int32_t *out = idx_out + bh * (int64_t)m_max * kPage;
-    for (int e = threadIdx.x; e < m_max * kPage; e += kSelThreads) {
+    for (int e = threadIdx.x; e < m_max * kPage; e += kThreads) {
         const int i = e >> 4, r = e & 15;
         const int p = m == 0 ? -1 : all ? (i < pages ? i : -1) : prow[i];
         out[e] = (p >= 0 && p * kPage + r < n) ? p * kPage + r : -1;
@@ -239,8 +242,15 @@ hipError_t launch_quest_select(const QuestArgs &a, hipStream_t stream)
                        dim3(256), 0, stream, (const uint16_t *)a.summary, a.page_table, a.seq_lens,
                        (const uint16_t *)a.q, a.num_q_heads, a.num_kv_heads, group, head_blocks, a.max_pages, keys,
                        stride);
-    hipLaunchKernelGGL(quest_select_kernel, dim3(a.num_q_heads, a.batch), dim3(kSelThreads), 0, stream, keys,
-                       stride, a.seq_lens, a.pages_per_seq, a.num_q_heads, a.pages_max, pages_tmp, a.idx_out);
+    // Fewer rows than CUs with long page lists: twice the threads per row (as for the
+    // token select).
+    const dim3 sgrid(a.num_q_heads, a.batch);
+    if ((int64_t)a.num_q_heads * a.batch < kCUs && pages_used >= 4096)
+        hipLaunchKernelGGL(quest_select_kernel<1024>, sgrid, dim3(1024), 0, stream, keys, stride, a.seq_lens,
+                           a.pages_per_seq, a.num_q_heads, a.pages_max, pages_tmp, a.idx_out);
+    else
+        hipLaunchKernelGGL(quest_select_kernel<kSelThreads>, sgrid, dim3(kSelThreads), 0, stream, keys, stride,
+                           a.seq_lens, a.pages_per_seq, a.num_q_heads, a.pages_max, pages_tmp, a.idx_out);
     return hipGetLastError();
 }
 

@@ -94,6 +94,15 @@ def test_quest_configs(cfg, kw, m):
     check_quest(dev, oracle.Cache.of(wl), wl.q, m_per_seq, m, tag=f"C{cfg}-quest")
 
 
+def test_quest_long_rows_few_rows():
+    """Fewer rows than CUs with page lists of 4096 pages or more take the wide page
+    selection (twice the threads per row): the long-retrieval shape with 2 sequences."""
+    wl = synth.config(3, n=70000, batch=2)
+    dev = DeviceCase.of_workload(wl)
+    m_per_seq = np.array([300, 87], np.int32)
+    check_quest(dev, oracle.Cache.of(wl), wl.q, m_per_seq, 300, tag="C3-long-quest")
+
+
 def test_quest_integer_strict_and_edges():
     """Integer inputs: exact bounds, many ties (lower page first); budgets of 0, 1,
     a ragged middle and more than the row holds."""
