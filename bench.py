@@ -152,7 +152,7 @@ def quest_leg(sdi, wl, kv_full, step_args, timed_graph, per, reps, n_q, k_max, i
     qidx = torch.empty((B, hq, 16 * pages_max), dtype=torch.int32, device=dev)
     ws_q = torch.empty(max(1, sdi.load_library().sparse_decode_quest_select_workspace(
         ctypes.byref(kv_full.struct()), hq, pages_max)), dtype=torch.uint8, device=dev)
-    ws_qa = torch.empty(max(1, sdi.attend_workspace_bytes(kv_full, hq, 16 * pages_max)), dtype=torch.uint8,
+    ws_qa = torch.zeros(max(1, sdi.attend_workspace_bytes(kv_full, hq, 16 * pages_max)), dtype=torch.uint8,
                         device=dev)
 
     def update(s):
@@ -292,7 +292,7 @@ def sampled_leg(sdi, wl, kv_full, step_args, timed_graph, per, reps, n_q, k_max,
     kidx = torch.empty((B, hq, kd_max), dtype=torch.int32, device=dev)
     sample = torch.empty((B, hq, s_max), dtype=torch.int32, device=dev)
     weight = torch.empty((B, hq), dtype=torch.float32, device=dev)
-    ws_s = torch.empty(max(1, sdi.attend_sampled_workspace_bytes(kv_full, hq, kd_max, s_max)), dtype=torch.uint8,
+    ws_s = torch.zeros(max(1, sdi.attend_sampled_workspace_bytes(kv_full, hq, kd_max, s_max)), dtype=torch.uint8,
                        device=dev)
 
     def index(s):
@@ -389,7 +389,7 @@ def main():
     idx = torch.empty((B, hq, k_max), dtype=torch.int32, device=dev)
     out = torch.empty((B, hq, 128), dtype=torch.float32, device=dev)
     ws_index = torch.empty(max(1, sdi.index_topk_workspace_bytes(kv_full, hq, k_max)), dtype=torch.uint8, device=dev)
-    ws_attend = torch.empty(max(1, sdi.attend_workspace_bytes(kv_full, hq, k_max)), dtype=torch.uint8, device=dev)
+    ws_attend = torch.zeros(max(1, sdi.attend_workspace_bytes(kv_full, hq, k_max)), dtype=torch.uint8, device=dev)
     ws_dense = torch.empty(max(1, sdi.dense_workspace_bytes(kv_full, hq)), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
     setup_s = time.perf_counter() - t_setup

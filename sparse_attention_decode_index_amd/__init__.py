@@ -118,15 +118,47 @@ def _stream(stream) -> Optional[int]:
     return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
 
 
-def _check(t, name, dtype, ndim):
+def _check(t, name, dtype, ndim, shape=None, min_len=None):
+    """Type, rank, shape and layout of one tensor argument.  `shape` lists the expected
+    sizes (None = any); `min_len` is a lower bound on a 1-d tensor's length.  The C ABI
+    cannot see tensor sizes, so a mismatch caught here is what stops a kernel from
+    reading or writing past a buffer.  Every entry point checks all shapes first and the
+    devices last (_on_device)."""
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if t.dim() != ndim:
         raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+    if shape is not None:
+        for got, want in zip(t.shape, shape):
+            if want is not None and int(got) != int(want):
+                want_s = tuple("*" if w is None else int(w) for w in shape)
+                raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {want_s}")
+    if min_len is not None and int(t.shape[0]) < int(min_len):
+        raise ValueError(f"{name} holds {int(t.shape[0])} entries, needs at least {int(min_len)} (one per sequence)")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
-    if not t.is_cuda:
-        raise ValueError(f"{name} must be a device tensor")
+
+
+def _on_device(**tensors):
+    for name, t in tensors.items():
+        if t is not None and not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+
+
+def _check_q(kv, q):
+    """q must be bf16 [batch][Hq][128] with Hq a multiple of the kv heads; returns Hq."""
+    import torch
+    _check(q, "q", torch.bfloat16, 3, (kv.batch, None, HEAD_DIM))
+    hq = int(q.shape[1])
+    if hq < 1 or hq % kv.num_kv_heads != 0:
+        raise ValueError(f"q has {hq} heads, not a positive multiple of the cache's {kv.num_kv_heads} kv heads")
+    return hq
+
+
+def _check_counts(kv, t, name):
+    import torch
+    if t is not None:
+        _check(t, name, torch.int32, 1, min_len=kv.batch)
 
 
 class PagedKV:
@@ -135,15 +167,16 @@ class PagedKV:
 
     def __init__(self, k_cache, v_cache, page_table, seq_lens, n_max: Optional[int] = None):
         import torch
-        _check(k_cache, "k_cache", torch.bfloat16, 4)
+        _check(k_cache, "k_cache", torch.bfloat16, 4, (None, None, PAGE_SIZE, HEAD_DIM))
         if v_cache is not None:
-            _check(v_cache, "v_cache", torch.bfloat16, 4)
-            if v_cache.shape != k_cache.shape:
-                raise ValueError("k_cache and v_cache shapes differ")
+            _check(v_cache, "v_cache", torch.bfloat16, 4, tuple(k_cache.shape))
         _check(page_table, "page_table", torch.int32, 2)
-        _check(seq_lens, "seq_lens", torch.int32, 1)
+        _check(seq_lens, "seq_lens", torch.int32, 1, (page_table.shape[0],))
+        _on_device(k_cache=k_cache, v_cache=v_cache, page_table=page_table, seq_lens=seq_lens)
         self.k_cache, self.v_cache, self.page_table, self.seq_lens = k_cache, v_cache, page_table, seq_lens
         self.n_max = int(seq_lens.max().item()) if n_max is None else int(n_max)
+        if self.n_max > int(page_table.shape[1]) * PAGE_SIZE:
+            raise ValueError(f"n_max {self.n_max} needs more than the page table's {int(page_table.shape[1])} pages")
 
     @property
     def batch(self) -> int:
@@ -180,23 +213,42 @@ def dense_workspace_bytes(kv: PagedKV, num_q_heads: int) -> int:
     return int(load_library().dense_decode_workspace(ctypes.byref(s), num_q_heads))
 
 
-def _workspace(nbytes: int, device, workspace):
+def _workspace(nbytes: int, device, workspace, zeroed: bool = False):
+    """The caller's workspace (checked for size), or a new one.  zeroed: the call keeps
+    per-row counters at the head of its workspace that must be zero when it starts (the
+    attend calls); a new workspace is then allocated zeroed."""
     import torch
     if workspace is not None:
         if workspace.numel() * workspace.element_size() < nbytes:
             raise ValueError(f"workspace holds {workspace.numel() * workspace.element_size()} bytes, needs {nbytes}")
         return workspace
+    if zeroed:
+        return torch.zeros(max(nbytes, 1), dtype=torch.uint8, device=device)
     return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+
+
+def attend_workspace(kv: PagedKV, num_q_heads: int, k_max: int, s_max: int = 0, device=None):
+    """A zeroed workspace for attend (s_max = 0) or attend_sampled: its per-row merge
+    counters start at zero, and every call leaves them at zero, so one workspace serves
+    any number of calls with the same or a smaller batch x heads."""
+    import torch
+    s = kv.struct()
+    lib = load_library()
+    n = (lib.sparse_decode_attend_workspace(ctypes.byref(s), num_q_heads, k_max) if s_max == 0 else
+         lib.sparse_decode_attend_sampled_workspace(ctypes.byref(s), num_q_heads, k_max, s_max))
+    return torch.zeros(max(int(n), 1), dtype=torch.uint8, device=device or kv.k_cache.device)
 
 
 def index_topk(kv: PagedKV, q, k_per_seq, k_max: int, idx_out=None, workspace=None, stream=None):
     """Exact top-k per (b, query head): int32 [B][Hq][k_max], ascending, -1 padded."""
     import torch
-    _check(q, "q", torch.bfloat16, 3)
-    _check(k_per_seq, "k_per_seq", torch.int32, 1)
-    B, hq, _ = q.shape
+    hq = _check_q(kv, q)
+    _check(k_per_seq, "k_per_seq", torch.int32, 1, min_len=kv.batch)
+    B = kv.batch
     if idx_out is None:
         idx_out = torch.empty((B, hq, k_max), dtype=torch.int32, device=q.device)
+    _check(idx_out, "idx_out", torch.int32, 3, (B, hq, k_max))
+    _on_device(q=q, k_per_seq=k_per_seq, idx_out=idx_out)
     s = kv.struct()
     lib = load_library()
     ws = _workspace(lib.sparse_decode_index_topk_workspace(ctypes.byref(s), hq, k_max), q.device, workspace)
@@ -211,17 +263,18 @@ def attend(kv: PagedKV, q, idx, k_per_seq=None, softmax_scale: float = DEFAULT_S
            workspace=None, stream=None):
     """Softmax attention over the listed rows: fp32 [B][Hq][128]."""
     import torch
-    _check(q, "q", torch.bfloat16, 3)
-    _check(idx, "idx", torch.int32, 3)
-    if k_per_seq is not None:
-        _check(k_per_seq, "k_per_seq", torch.int32, 1)
-    B, hq, _ = q.shape
+    hq = _check_q(kv, q)
+    B = kv.batch
+    _check(idx, "idx", torch.int32, 3, (B, hq, None))
+    _check_counts(kv, k_per_seq, "k_per_seq")
     k_max = int(idx.shape[2])
     if out is None:
         out = torch.empty((B, hq, HEAD_DIM), dtype=torch.float32, device=q.device)
+    _check(out, "out", torch.float32, 3, (B, hq, HEAD_DIM))
+    _on_device(q=q, idx=idx, k_per_seq=k_per_seq, out=out)
     s = kv.struct()
     lib = load_library()
-    ws = _workspace(lib.sparse_decode_attend_workspace(ctypes.byref(s), hq, k_max), q.device, workspace)
+    ws = _workspace(lib.sparse_decode_attend_workspace(ctypes.byref(s), hq, k_max), q.device, workspace, zeroed=True)
     rc = lib.sparse_decode_attend(ctypes.byref(s), _ptr(q), hq, _ptr(idx), _ptr(k_per_seq), k_max,
                                   float(softmax_scale), _ptr(out), _ptr(ws), ws.numel() * ws.element_size(),
                                   _stream(stream))
@@ -233,10 +286,12 @@ def attend(kv: PagedKV, q, idx, k_per_seq=None, softmax_scale: float = DEFAULT_S
 def dense(kv: PagedKV, q, softmax_scale: float = DEFAULT_SCALE, out=None, workspace=None, stream=None):
     """Softmax attention over every cached token: fp32 [B][Hq][128]."""
     import torch
-    _check(q, "q", torch.bfloat16, 3)
-    B, hq, _ = q.shape
+    hq = _check_q(kv, q)
+    B = kv.batch
     if out is None:
         out = torch.empty((B, hq, HEAD_DIM), dtype=torch.float32, device=q.device)
+    _check(out, "out", torch.float32, 3, (B, hq, HEAD_DIM))
+    _on_device(q=q, out=out)
     s = kv.struct()
     lib = load_library()
     ws = _workspace(lib.dense_decode_workspace(ctypes.byref(s), hq), q.device, workspace)
@@ -263,8 +318,8 @@ def quest_summarize(kv: PagedKV, summary=None, current_pages_only: bool = False,
     if summary is None:
         summary = torch.empty((s.num_pages, s.num_kv_heads, 2, HEAD_DIM), dtype=torch.bfloat16,
                               device=kv.k_cache.device)
-    if summary.numel() * summary.element_size() < lib.sparse_decode_quest_summary_bytes(ctypes.byref(s)):
-        raise ValueError("summary buffer too small")
+    _check(summary, "summary", torch.bfloat16, 4, (s.num_pages, s.num_kv_heads, 2, HEAD_DIM))
+    _on_device(summary=summary)
     rc = lib.sparse_decode_quest_summarize(ctypes.byref(s), _ptr(summary), 1 if current_pages_only else 0,
                                            _stream(stream))
     if rc != SDI_OK:
@@ -277,12 +332,15 @@ def quest_select(kv: PagedKV, q, summary, pages_per_seq, pages_max: int, idx_out
     """Current page plus the highest-bound pages per (b, query head): token indices
     int32 [B][Hq][16 pages_max] (page by page, -1 past N_b or past the selection)."""
     import torch
-    _check(q, "q", torch.bfloat16, 3)
-    _check(pages_per_seq, "pages_per_seq", torch.int32, 1)
-    B, hq, _ = q.shape
+    hq = _check_q(kv, q)
+    _check(pages_per_seq, "pages_per_seq", torch.int32, 1, min_len=kv.batch)
+    B = kv.batch
+    s = kv.struct()
+    _check(summary, "summary", torch.bfloat16, 4, (s.num_pages, s.num_kv_heads, 2, HEAD_DIM))
     if idx_out is None:
         idx_out = torch.empty((B, hq, 16 * pages_max), dtype=torch.int32, device=q.device)
-    s = kv.struct()
+    _check(idx_out, "idx_out", torch.int32, 3, (B, hq, 16 * pages_max))
+    _on_device(q=q, pages_per_seq=pages_per_seq, summary=summary, idx_out=idx_out)
     lib = load_library()
     ws = _workspace(lib.sparse_decode_quest_select_workspace(ctypes.byref(s), hq, pages_max), q.device, workspace)
     rc = lib.sparse_decode_quest_select(ctypes.byref(s), _ptr(q), hq, _ptr(summary), _ptr(pages_per_seq),
@@ -297,13 +355,13 @@ def label_build(kv: PagedKV, channels, labels=None, current_pages_only: bool = F
     """Label rows bf16 [num_pages][Hkv][16][16]: channels (int32 [Hkv][16], device) of
     every cached key row.  With current_pages_only, only each sequence's last page."""
     import torch
-    _check(channels, "channels", torch.int32, 2)
     s = kv.struct()
+    _check(channels, "channels", torch.int32, 2, (s.num_kv_heads, 16))
     lib = load_library()
     if labels is None:
         labels = torch.empty((s.num_pages, s.num_kv_heads, 16, 16), dtype=torch.bfloat16, device=kv.k_cache.device)
-    if labels.numel() * labels.element_size() < lib.sparse_decode_label_bytes(ctypes.byref(s)):
-        raise ValueError("label buffer too small")
+    _check(labels, "labels", torch.bfloat16, 4, (s.num_pages, s.num_kv_heads, 16, 16))
+    _on_device(channels=channels, labels=labels)
     rc = lib.sparse_decode_label_build(ctypes.byref(s), _ptr(channels), _ptr(labels),
                                        1 if current_pages_only else 0, _stream(stream))
     if rc != SDI_OK:
@@ -315,13 +373,16 @@ def label_index_topk(kv: PagedKV, q, labels, channels, k_per_seq, k_max: int, id
                      stream=None):
     """Top-k per (b, query head) of the reduced-channel scores: int32 [B][Hq][k_max]."""
     import torch
-    _check(q, "q", torch.bfloat16, 3)
-    _check(k_per_seq, "k_per_seq", torch.int32, 1)
-    _check(channels, "channels", torch.int32, 2)
-    B, hq, _ = q.shape
+    hq = _check_q(kv, q)
+    _check(k_per_seq, "k_per_seq", torch.int32, 1, min_len=kv.batch)
+    B = kv.batch
+    s = kv.struct()
+    _check(channels, "channels", torch.int32, 2, (s.num_kv_heads, 16))
+    _check(labels, "labels", torch.bfloat16, 4, (s.num_pages, s.num_kv_heads, 16, 16))
     if idx_out is None:
         idx_out = torch.empty((B, hq, k_max), dtype=torch.int32, device=q.device)
-    s = kv.struct()
+    _check(idx_out, "idx_out", torch.int32, 3, (B, hq, k_max))
+    _on_device(q=q, k_per_seq=k_per_seq, channels=channels, labels=labels, idx_out=idx_out)
     lib = load_library()
     ws = _workspace(lib.sparse_decode_index_topk_workspace(ctypes.byref(s), hq, k_max), q.device, workspace)
     rc = lib.sparse_decode_label_index_topk(ctypes.byref(s), _ptr(q), hq, _ptr(labels), _ptr(channels),
@@ -337,18 +398,25 @@ def sample_residual(kv: PagedKV, idx, k_per_seq, draws, s_per_seq, sample_out=No
     weight fp32 [B][Hq]).  draws: 32-bit random numbers [B][Hq][s_max] (uint32, or
     their bits in int32)."""
     import torch
-    _check(idx, "idx", torch.int32, 3)
-    _check(k_per_seq, "k_per_seq", torch.int32, 1)
-    _check(s_per_seq, "s_per_seq", torch.int32, 1)
-    if draws.dtype not in (torch.int32, torch.uint32) or draws.dim() != 3 or not draws.is_contiguous() \
-            or not draws.is_cuda:
-        raise ValueError("draws must be a contiguous 3-d int32 or uint32 device tensor")
-    B, hq, k_max = idx.shape
+    _check(idx, "idx", torch.int32, 3, (kv.batch, None, None))
+    _check(k_per_seq, "k_per_seq", torch.int32, 1, min_len=kv.batch)
+    _check(s_per_seq, "s_per_seq", torch.int32, 1, min_len=kv.batch)
+    B, hq, k_max = (int(x) for x in idx.shape)
+    if hq < 1 or hq % kv.num_kv_heads != 0:
+        raise ValueError(f"idx has {hq} heads, not a positive multiple of the cache's {kv.num_kv_heads} kv heads")
+    if draws.dtype not in (torch.int32, torch.uint32) or draws.dim() != 3 or not draws.is_contiguous():
+        raise ValueError("draws must be a contiguous 3-d int32 or uint32 tensor")
+    if tuple(draws.shape[:2]) != (B, hq):
+        raise ValueError(f"draws has shape {tuple(draws.shape)}, expected ({B}, {hq}, *)")
     s_max = int(draws.shape[2])
     if sample_out is None:
         sample_out = torch.empty((B, hq, s_max), dtype=torch.int32, device=idx.device)
     if weight_out is None:
         weight_out = torch.empty((B, hq), dtype=torch.float32, device=idx.device)
+    _check(sample_out, "sample_out", torch.int32, 3, (B, hq, s_max))
+    _check(weight_out, "weight_out", torch.float32, 2, (B, hq))
+    _on_device(idx=idx, k_per_seq=k_per_seq, s_per_seq=s_per_seq, draws=draws, sample_out=sample_out,
+               weight_out=weight_out)
     s = kv.struct()
     rc = load_library().sparse_decode_sample_residual(ctypes.byref(s), hq, _ptr(idx), _ptr(k_per_seq), k_max,
                                                       _ptr(draws), _ptr(s_per_seq), s_max, _ptr(sample_out),
@@ -363,22 +431,23 @@ def attend_sampled(kv: PagedKV, q, idx, k_per_seq, sample, sample_weight, s_per_
     """The stochastic estimate: softmax sums over idx (weight 1) and sample (weight
     sample_weight[b, h] per entry): fp32 [B][Hq][128]."""
     import torch
-    _check(q, "q", torch.bfloat16, 3)
-    _check(idx, "idx", torch.int32, 3)
-    if k_per_seq is not None:
-        _check(k_per_seq, "k_per_seq", torch.int32, 1)
-    if s_per_seq is not None:
-        _check(s_per_seq, "s_per_seq", torch.int32, 1)
-    _check(sample, "sample", torch.int32, 3)
-    _check(sample_weight, "sample_weight", torch.float32, 2)
-    B, hq, _ = q.shape
+    hq = _check_q(kv, q)
+    B = kv.batch
+    _check(idx, "idx", torch.int32, 3, (B, hq, None))
+    _check_counts(kv, k_per_seq, "k_per_seq")
+    _check_counts(kv, s_per_seq, "s_per_seq")
+    _check(sample, "sample", torch.int32, 3, (B, hq, None))
+    _check(sample_weight, "sample_weight", torch.float32, 2, (B, hq))
     k_max, s_max = int(idx.shape[2]), int(sample.shape[2])
     if out is None:
         out = torch.empty((B, hq, HEAD_DIM), dtype=torch.float32, device=q.device)
+    _check(out, "out", torch.float32, 3, (B, hq, HEAD_DIM))
+    _on_device(q=q, idx=idx, k_per_seq=k_per_seq, s_per_seq=s_per_seq, sample=sample,
+               sample_weight=sample_weight, out=out)
     s = kv.struct()
     lib = load_library()
     ws = _workspace(lib.sparse_decode_attend_sampled_workspace(ctypes.byref(s), hq, k_max, s_max), q.device,
-                    workspace)
+                    workspace, zeroed=True)
     rc = lib.sparse_decode_attend_sampled(ctypes.byref(s), _ptr(q), hq, _ptr(idx), _ptr(k_per_seq), k_max,
                                           _ptr(sample), _ptr(sample_weight), _ptr(s_per_seq), s_max,
                                           float(softmax_scale), _ptr(out), _ptr(ws), ws.numel() * ws.element_size(),

@@ -41,7 +41,6 @@
 #include "sdi_radix.hpp"
 #include "sdi_index.hpp"
 
-#include <atomic>
 #include <cmath>
 #include <type_traits>
 
@@ -799,19 +798,12 @@ template <int kThreads>
 static hipError_t launch_select_with(const SelectArgs &s, const SelectPlan &p, int batch, hipStream_t stream)
 {
     if (p.dyn > 64 * 1024) {
-        // raise the kernel's dynamic-LDS limit to the budget once per device (a function
-        // attribute, not a stream operation)
-        static std::atomic<uint64_t> raised{0};
-        int dev = 0;
-        hipError_t e = hipGetDevice(&dev);
+        // raise the kernel's dynamic-LDS limit to the budget (a function attribute kept by
+        // the runtime, not a stream operation; setting it again is harmless and keeps the
+        // library free of state of its own)
+        const hipError_t e = hipFuncSetAttribute((const void *)select_kernel<kThreads>,
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, kSelDynMax);
         if (e != hipSuccess) return e;
-        const uint64_t bit = dev < 64 ? (uint64_t)1 << dev : 0;
-        if (bit == 0 || !(raised.load(std::memory_order_acquire) & bit)) {
-            e = hipFuncSetAttribute((const void *)select_kernel<kThreads>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                    kSelDynMax);
-            if (e != hipSuccess) return e;
-            raised.fetch_or(bit, std::memory_order_acq_rel);
-        }
     }
     hipLaunchKernelGGL(select_kernel<kThreads>, dim3(s.num_q_heads, batch), dim3(kThreads), p.dyn, stream, s);
     return hipGetLastError();

@@ -34,6 +34,19 @@ class DeviceCase:
     def of_tiny(cls, case, device="cuda"):
         return cls(case.k_cache, case.v_cache, case.page_table, case.lens, case.q, device)
 
+    def append(self, rows, q_bits, n_max):
+        """Append one token per sequence with plain device copies (the cache-growth step
+        of a decode loop): rows = (tok, pages, slots, k_rows, v_rows) as
+        synth.Workload.new_rows returns them; then install the next step's queries."""
+        tok, pages, slots, kr, vr = rows
+        p = torch.from_numpy(np.asarray(pages)).to(self.k.device)
+        s = torch.from_numpy(np.asarray(slots)).to(self.k.device)
+        self.k[p, :, s, :] = bf16_tensor(kr, self.k.device)
+        self.v[p, :, s, :] = bf16_tensor(vr, self.k.device)
+        self.sl += 1
+        self.q.copy_(bf16_tensor(q_bits, self.k.device))
+        self.kv = sdi.PagedKV(self.k, self.v, self.pt, self.sl, n_max=int(n_max))
+
     def index(self, k_per_seq, k_max):
         idx = sdi.index_topk(self.kv, self.q, i32_tensor(k_per_seq), k_max)
         torch.cuda.synchronize()

@@ -2,8 +2,8 @@
 
 Sizes are ones the oracle finishes in seconds yet span several score chunks
 (1024 tokens), several attend chunks (256 indices) and a ragged tail; the
-full-size decode layer that the benchmark times is checked on sampled
-sequences.  Comparison rules are in tests/parity.py.
+full-size workloads are in test_gpu_full_size.py.  Comparison rules are in
+tests/parity.py.
 """
 import numpy as np
 import pytest
@@ -81,16 +81,6 @@ def test_two_slot_workgroups(cfg, kw):
     run_and_check(dev, oracle.Cache.of(wl), wl.q, wl.k_per_seq(), wl.k_max(), tag=f"C{cfg}-two-slot")
 
 
-def _append_on_device(dev, rows):
-    tok, pages, slots, kr, vr = rows
-    from device import bf16_tensor
-    p = torch.from_numpy(pages).cuda()
-    s = torch.from_numpy(slots).cuda()
-    dev.k[p, :, s, :] = bf16_tensor(kr)
-    dev.v[p, :, s, :] = bf16_tensor(vr)
-    dev.sl += 1
-
-
 @pytest.mark.parametrize("cfg,kw,ratios", [
     (4, dict(n=5000, batch=2, steps=3), (100, 50, 20, 1)),
     (5, dict(n=6000, batch=6, steps=3), (50,)),
@@ -103,9 +93,7 @@ def test_multi_step_growth(cfg, kw, ratios):
     for step in range(wl.steps):
         if step > 0:
             rows = wl.advance()                          # host copy for the oracle
-            _append_on_device(dev, rows)
-            dev.q.copy_(torch.from_numpy(wl.q.view(np.int16)).cuda().view(torch.bfloat16))
-            dev.kv = sdi.PagedKV(dev.k, dev.v, dev.pt, dev.sl, n_max=wl.n_max)
+            dev.append(rows, wl.q, wl.n_max)
         cache = oracle.Cache.of(wl)
         for r in ratios:
             rule = synth.k_ceil(r) if cfg == 5 else synth.k_half_up(r)
@@ -269,38 +257,7 @@ def test_workspace_too_small_is_rejected():
         sdi.index_topk(dev.kv, dev.q, i32_tensor(wl.k_per_seq()), 82, workspace=ws)
 
 
-# ------------------------------------------------------------------------ full size, sampled
-
-@pytest.mark.parametrize("cfg,ratio,sample", [(2, None, [0, 5]), (3, None, [2]), (4, 20, [7]), (5, None, [4, 17])],
-                         ids=["C2-full", "C3-full", "C4-full-k=N/20", "C5-full"])
-def test_full_size_sampled(cfg, ratio, sample):
-    """The full decode layer in the benchmark's launch configuration; the oracle checks
-    every head of the sampled sequences, and properties are checked for every row.  The
-    sweep runs at its most crowded candidate-path budget (k = N/20); the agentic batch
-    at its first step (its ragged rows, fragmented pages and per-sequence k)."""
-    wl = synth.config(cfg, ratio=ratio)
-    dev = DeviceCase.of_workload(wl)
-    kps = wl.k_per_seq()
-    k_max = wl.k_max()
-    _say(f"[case] C{cfg} full size: index/attend/dense on the GPU")
-    gidx = dev.index(kps, k_max)
-    out = dev.attend(gidx, kps)
-    dn = dev.dense()
-    for b in range(wl.batch):                               # properties on every row
-        for h in range(wl.num_q_heads):
-            row = gidx[b, h]
-            assert np.all(np.diff(row[:kps[b]]) > 0) and row[0] >= 0 and row[kps[b] - 1] < wl.seq_lens[b]
-            if cfg == 2:
-                assert set(wl.meta["planted_positions"][(b, h // 4)]) <= set(row.tolist())
-    sub = np.array(sample)
-    cache = oracle.Cache(wl.k_cache, wl.v_cache, wl.page_table[sub], wl.seq_lens[sub], wl.num_kv_heads)
-    q = wl.q[sub]
-    s = oracle.scores(cache, q)
-    oidx, kth = oracle.topk(s, cache.sl, kps[sub], k_max)
-    check_indices(gidx[sub], oidx, s, kth, cache.sl, kps[sub])
-    check_close(out[sub], oracle.attend(cache, q, gidx[sub]), what=f"C{cfg} attend")
-    check_close(dn[sub], oracle.dense(cache, q), what=f"C{cfg} dense")
-
+# ------------------------------------------------------------------------ long rows and select paths
 
 def test_long_rows_many_slots():
     """Rows of more than 512 slots (262144 tokens): the select reads the slot headers in
@@ -411,7 +368,7 @@ def test_graph_replay_matches_eager():
     out = torch.empty((B, hq, 128), dtype=torch.float32, device="cuda")
     dn = torch.empty_like(out)
     ws_i = torch.empty(sdi.index_topk_workspace_bytes(dev.kv, hq, k_max), dtype=torch.uint8, device="cuda")
-    ws_a = torch.empty(max(1, sdi.attend_workspace_bytes(dev.kv, hq, k_max)), dtype=torch.uint8, device="cuda")
+    ws_a = torch.zeros(max(1, sdi.attend_workspace_bytes(dev.kv, hq, k_max)), dtype=torch.uint8, device="cuda")
     ws_d = torch.empty(sdi.dense_workspace_bytes(dev.kv, hq), dtype=torch.uint8, device="cuda")
 
     def step():
