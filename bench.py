@@ -28,21 +28,26 @@ sys.path.insert(0, ROOT)
 
 METRIC = "decode steps/s + effective HBM GB/s (% of peak) at 50x sparsity vs dense"
 PEAK_HBM_BPS = 8.0e12          # MI355X HBM3E peak
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_index_topk_C2.txt")
+FLUSH_BYTES = 1 << 30          # written before a cold launch: flushes the 256 MB Infinity Cache and the L2s
+
+
+def traffic_file(cfg):
+    return os.path.join(ROOT, "profiles", f"traffic_index_topk_C{cfg}.txt")
 
 
 def parse_args():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", type=int, default=2, help="decode configuration 1-5 (default 2)")
+    ap.add_argument("--steps", type=int, default=64)
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--config", type=int, default=5,
+                    help="decode configuration 1-5 (default 5, the agentic ragged batch: the largest 50x workload)")
     ap.add_argument("--ratio", type=int, default=50, help="sparsity N/k (default 50)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-cold", action="store_true",
-                    help="skip timing each launch group after a 1 GiB cache flush (eager launches)")
+                    help="skip timing each launch group after a 1 GiB cache flush")
     ap.add_argument("--mode", choices=("graph", "eager"), default="graph",
                     help="replay captured HIP graphs (default) or launch eagerly from Python")
     ap.add_argument("--quest", action="store_true",
@@ -57,6 +62,9 @@ def parse_args():
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="after timing, copy a buffer of this many MiB 3 times (a plain device copy of known "
                          "size, the reference for scaling memory-traffic counters)")
+    ap.add_argument("--trace-summary", metavar="DIR",
+                    help="no benchmark: summarise the rocprofv3 output under DIR (kernel trace, and counters "
+                         "when collected) of an earlier run of this script, per kernel, warm and cold")
     return ap.parse_args()
 
 
@@ -72,12 +80,13 @@ def algorithmic_bytes(seq_lens, kps, B, hq, hkv):
     return index, attend, dense
 
 
-def read_traffic():
+def read_traffic(cfg):
     """HBM bytes per launch of the indexer from the committed counter summary, if any."""
-    if not os.path.exists(TRAFFIC_FILE):
+    path = traffic_file(cfg)
+    if not os.path.exists(path):
         return None
     vals = {}
-    for line in open(TRAFFIC_FILE):
+    for line in open(path):
         if ":" in line and not line.lstrip().startswith("#"):
             key, val = line.split(":", 1)
             vals[key.strip()] = val.strip()
@@ -93,6 +102,67 @@ def source_sha():
     for f in ("index_topk.hip", "sdi_device.hpp", "sdi_radix.hpp", "sdi_index.hpp"):
         h.update(open(os.path.join(ROOT, "sparse_attention_decode_index_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
+
+
+def trace_summary(root):
+    """Per-kernel durations from a rocprofv3 kernel trace (CSV) of a run of this script:
+    warm launches, and cold ones -- the first launch of each library kernel after a
+    1 GiB cache-flush fill (torch's uint8 FillFunctor taking over 50 us).  With counter
+    collection output present, the counters per dispatch as well."""
+    import csv
+    import glob
+    import statistics as st
+    traces = sorted(glob.glob(os.path.join(root, "**", "*kernel_trace.csv"), recursive=True))
+    if not traces:
+        sys.exit(f"no *kernel_trace.csv under {root}")
+    rows = []
+    for path in traces:
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                rows.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), r["Kernel_Name"]))
+    rows.sort()
+
+    def short(name):
+        name = name.split("(")[0] if name.startswith("void ") else name
+        return name.replace("void ", "")
+
+    warm, cold = {}, {}
+    seen = None                                  # library kernels met since the last flush
+    for t0, t1, name in rows:
+        us = (t1 - t0) / 1e3
+        if "FillFunctor<unsigned char>" in name and us > 50.0:
+            seen = set()
+            continue
+        if "sdi::" not in name:
+            continue
+        k = short(name)
+        if seen is not None and k not in seen:   # the first launch of this kernel after a flush
+            seen.add(k)
+            cold.setdefault(k, []).append(us)
+        else:
+            warm.setdefault(k, []).append(us)
+    out = {"kernels": {}}
+    for k in sorted(set(warm) | set(cold), key=lambda n: -sum(warm.get(n, [0.0]))):
+        v = warm.get(k, [])
+        e = {"calls": len(v), "avg_us": st.mean(v), "min_us": min(v), "max_us": max(v)} if v else {"calls": 0}
+        c = cold.get(k, [])
+        if c:
+            e.update({"cold_calls": len(c), "cold_avg_us": st.mean(c), "cold_median_us": st.median(c)})
+        out["kernels"][k] = e
+    counters = sorted(glob.glob(os.path.join(root, "**", "*counter_collection.csv"), recursive=True))
+    if counters:
+        per = {}
+        for path in counters:
+            with open(path) as f:
+                for r in csv.DictReader(f):
+                    name = short(r.get("Kernel_Name", ""))
+                    key = (name, r.get("Counter_Name", ""))
+                    per.setdefault(key, {}).setdefault(r.get("Dispatch_Id", ""), 0.0)
+                    per[key][r.get("Dispatch_Id", "")] += float(r.get("Counter_Value", 0.0))
+        out["counters_per_dispatch_kib"] = {
+            f"{n} {c}": {"dispatches": len(d), "mean": st.mean(d.values()), "min": min(d.values()),
+                         "max": max(d.values())} for (n, c), d in sorted(per.items())}
+    print(json.dumps(out, indent=1))
 
 
 def cpu_baseline(wl, target_s):
@@ -152,7 +222,7 @@ def quest_leg(sdi, wl, kv_full, step_args, timed_graph, per, reps, n_q, k_max, i
     qidx = torch.empty((B, hq, 16 * pages_max), dtype=torch.int32, device=dev)
     ws_q = torch.empty(max(1, sdi.load_library().sparse_decode_quest_select_workspace(
         ctypes.byref(kv_full.struct()), hq, pages_max)), dtype=torch.uint8, device=dev)
-    ws_qa = torch.zeros(max(1, sdi.attend_workspace_bytes(kv_full, hq, 16 * pages_max)), dtype=torch.uint8,
+    ws_qa = torch.empty(max(1, sdi.attend_workspace_bytes(kv_full, hq, 16 * pages_max)), dtype=torch.uint8,
                         device=dev)
 
     def update(s):
@@ -292,7 +362,7 @@ def sampled_leg(sdi, wl, kv_full, step_args, timed_graph, per, reps, n_q, k_max,
     kidx = torch.empty((B, hq, kd_max), dtype=torch.int32, device=dev)
     sample = torch.empty((B, hq, s_max), dtype=torch.int32, device=dev)
     weight = torch.empty((B, hq), dtype=torch.float32, device=dev)
-    ws_s = torch.zeros(max(1, sdi.attend_sampled_workspace_bytes(kv_full, hq, kd_max, s_max)), dtype=torch.uint8,
+    ws_s = torch.empty(max(1, sdi.attend_sampled_workspace_bytes(kv_full, hq, kd_max, s_max)), dtype=torch.uint8,
                        device=dev)
 
     def index(s):
@@ -345,6 +415,9 @@ def sampled_leg(sdi, wl, kv_full, step_args, timed_graph, per, reps, n_q, k_max,
 
 def main():
     args = parse_args()
+    if args.trace_summary:
+        trace_summary(args.trace_summary)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: the sparse decode path here has no multi-GPU mode "
               f"(asked for --gpus {args.gpus}).", file=sys.stderr)
@@ -389,7 +462,7 @@ def main():
     idx = torch.empty((B, hq, k_max), dtype=torch.int32, device=dev)
     out = torch.empty((B, hq, 128), dtype=torch.float32, device=dev)
     ws_index = torch.empty(max(1, sdi.index_topk_workspace_bytes(kv_full, hq, k_max)), dtype=torch.uint8, device=dev)
-    ws_attend = torch.zeros(max(1, sdi.attend_workspace_bytes(kv_full, hq, k_max)), dtype=torch.uint8, device=dev)
+    ws_attend = torch.empty(max(1, sdi.attend_workspace_bytes(kv_full, hq, k_max)), dtype=torch.uint8, device=dev)
     ws_dense = torch.empty(max(1, sdi.dense_workspace_bytes(kv_full, hq)), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
     setup_s = time.perf_counter() - t_setup
@@ -521,23 +594,25 @@ def main():
 
     cold = {}
     if not args.no_cold and args.mode == "graph":
-        # the 256 MB Infinity Cache and the L2s flushed by writing 1 GiB before each
-        # step; eager launches, so the figures include the host's launch gaps
-        flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-        ci, ca = [], []
-        for s in range(10):
-            flush.fill_(s & 0xFF)
-            e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-            run_step(s, e)
-            torch.cuda.synchronize()
-            ci.append(e[0].elapsed_time(e[1]) * 1e-3)
-            ca.append(e[1].elapsed_time(e[2]) * 1e-3)
-        cold = {"index_us_cold": float(np.median(ci) * 1e6), "attend_us_cold": float(np.median(ca) * 1e6)}
-        b_i, b_a, _ = algorithmic_bytes(wl.seq_lens, wl.k_per_seq(), B, hq, hkv)
-        cold["index_pct_of_peak_cold"] = 100 * b_i / (cold["index_us_cold"] * 1e-6) / PEAK_HBM_BPS
-        cold["attend_pct_of_peak_cold"] = 100 * b_a / (cold["attend_us_cold"] * 1e-6) / PEAK_HBM_BPS
-        del flush
+        # Each launch group right after writing 1 GiB (which flushes the 256 MB Infinity
+        # Cache and the L2s), inside HIP graphs: time(flush + group) - time(flush).
+        flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+        creps = max(1, min(reps, 4))
 
+        def flushed(body):
+            def run(s):
+                flush.fill_(s & 0xFF)
+                if body is not None:
+                    body(s)
+            return run
+        t_flush, _ = timed_graph(flushed(None), creps, per)
+        t_fi, _ = timed_graph(flushed(index_only), creps, per)
+        t_fa, _ = timed_graph(flushed(attend_only), creps, per)
+        t_fs, _ = timed_graph(flushed(full_step), creps, per)
+        cold = {"index_us_cold": (t_fi - t_flush) * 1e6, "attend_us_cold": (t_fa - t_flush) * 1e6,
+                "step_us_cold": (t_fs - t_flush) * 1e6,
+                "cold_timing": "graph replay: each group after a 1 GiB write, minus the write alone"}
+        del flush
     if args.calibration_copy_mib > 0:
         src = torch.ones(args.calibration_copy_mib << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -546,19 +621,28 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    kps0 = wl.k_per_seq()
-    b_index, b_attend, b_dense = algorithmic_bytes(wl.seq_lens, kps0, B, hq, hkv)
+    # algorithmic bytes per launch, averaged over the distinct steps the graphs replay
+    per_steps = per if args.mode == "graph" else 1
+    bytes_steps = [algorithmic_bytes((wl.seq_lens + (j if growth else 0)), kps_steps[j if growth else 0].cpu().numpy(),
+                                     B, hq, hkv) for j in range(per_steps)]
+    b_index, b_attend, b_dense = (float(np.mean([b[i] for b in bytes_steps])) for i in range(3))
     step_bytes = b_index + b_attend
+    if cold:
+        cold["index_pct_of_peak_cold"] = 100 * b_index / (cold["index_us_cold"] * 1e-6) / PEAK_HBM_BPS
+        cold["attend_pct_of_peak_cold"] = 100 * b_attend / (cold["attend_us_cold"] * 1e-6) / PEAK_HBM_BPS
     value = args.steps / wall
-    traffic = read_traffic()
+    traffic = read_traffic(args.config)
     roofline = {"bound": "hbm", "kernel": "index_topk (score_kernel + select_kernel)",
                 "achieved": b_index / mi / 1e9, "peak": PEAK_HBM_BPS / 1e9, "unit": "GB/s",
                 "frac": b_index / mi / PEAK_HBM_BPS, "traffic": traffic,
                 "algorithmic_bytes_per_launch": b_index, "avg_launch_us": mi * 1e6}
-    roofline_attend = {"bound": "hbm", "kernel": "attend (attend_kernel + merge_kernel)",
+    roofline_attend = {"bound": "hbm", "kernel": "attend_kernel",
                        "achieved": b_attend / ma / 1e9, "peak": PEAK_HBM_BPS / 1e9, "unit": "GB/s",
                        "frac": b_attend / ma / PEAK_HBM_BPS, "algorithmic_bytes_per_launch": b_attend,
                        "avg_launch_us": ma * 1e6}
+    if cold:
+        roofline["frac_cold"] = b_index / (cold["index_us_cold"] * 1e-6) / PEAK_HBM_BPS
+        roofline_attend["frac_cold"] = b_attend / (cold["attend_us_cold"] * 1e-6) / PEAK_HBM_BPS
     result = {
         "metric": METRIC, "value": value, "unit": "decode steps/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",

@@ -26,8 +26,9 @@
  *
  * Streams.  `stream` is a hipStream_t (NULL = the null stream).  Calls only
  * enqueue kernels; results are valid once the stream has reached them.  The
- * library holds no global state, so calls on different streams with different
- * workspaces may overlap; two in-flight calls must not share a workspace.
+ * library holds no state of its own between calls, so calls on different streams
+ * with different workspaces may overlap; two in-flight calls must not share a
+ * workspace.
  *
  * Errors.  Every check runs on the host before anything is enqueued; a call that
  * returns an error has enqueued nothing.  SDI_ERR_HIP reports a failed launch.

@@ -213,30 +213,13 @@ def dense_workspace_bytes(kv: PagedKV, num_q_heads: int) -> int:
     return int(load_library().dense_decode_workspace(ctypes.byref(s), num_q_heads))
 
 
-def _workspace(nbytes: int, device, workspace, zeroed: bool = False):
-    """The caller's workspace (checked for size), or a new one.  zeroed: the call keeps
-    per-row counters at the head of its workspace that must be zero when it starts (the
-    attend calls); a new workspace is then allocated zeroed."""
+def _workspace(nbytes: int, device, workspace):
     import torch
     if workspace is not None:
         if workspace.numel() * workspace.element_size() < nbytes:
             raise ValueError(f"workspace holds {workspace.numel() * workspace.element_size()} bytes, needs {nbytes}")
         return workspace
-    if zeroed:
-        return torch.zeros(max(nbytes, 1), dtype=torch.uint8, device=device)
     return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
-
-
-def attend_workspace(kv: PagedKV, num_q_heads: int, k_max: int, s_max: int = 0, device=None):
-    """A zeroed workspace for attend (s_max = 0) or attend_sampled: its per-row merge
-    counters start at zero, and every call leaves them at zero, so one workspace serves
-    any number of calls with the same or a smaller batch x heads."""
-    import torch
-    s = kv.struct()
-    lib = load_library()
-    n = (lib.sparse_decode_attend_workspace(ctypes.byref(s), num_q_heads, k_max) if s_max == 0 else
-         lib.sparse_decode_attend_sampled_workspace(ctypes.byref(s), num_q_heads, k_max, s_max))
-    return torch.zeros(max(int(n), 1), dtype=torch.uint8, device=device or kv.k_cache.device)
 
 
 def index_topk(kv: PagedKV, q, k_per_seq, k_max: int, idx_out=None, workspace=None, stream=None):
@@ -274,7 +257,7 @@ def attend(kv: PagedKV, q, idx, k_per_seq=None, softmax_scale: float = DEFAULT_S
     _on_device(q=q, idx=idx, k_per_seq=k_per_seq, out=out)
     s = kv.struct()
     lib = load_library()
-    ws = _workspace(lib.sparse_decode_attend_workspace(ctypes.byref(s), hq, k_max), q.device, workspace, zeroed=True)
+    ws = _workspace(lib.sparse_decode_attend_workspace(ctypes.byref(s), hq, k_max), q.device, workspace)
     rc = lib.sparse_decode_attend(ctypes.byref(s), _ptr(q), hq, _ptr(idx), _ptr(k_per_seq), k_max,
                                   float(softmax_scale), _ptr(out), _ptr(ws), ws.numel() * ws.element_size(),
                                   _stream(stream))
@@ -447,7 +430,7 @@ def attend_sampled(kv: PagedKV, q, idx, k_per_seq, sample, sample_weight, s_per_
     s = kv.struct()
     lib = load_library()
     ws = _workspace(lib.sparse_decode_attend_sampled_workspace(ctypes.byref(s), hq, k_max, s_max), q.device,
-                    workspace, zeroed=True)
+                    workspace)
     rc = lib.sparse_decode_attend_sampled(ctypes.byref(s), _ptr(q), hq, _ptr(idx), _ptr(k_per_seq), k_max,
                                           _ptr(sample), _ptr(sample_weight), _ptr(s_per_seq), s_max,
                                           float(softmax_scale), _ptr(out), _ptr(ws), ws.numel() * ws.element_size(),

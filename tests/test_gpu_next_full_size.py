@@ -145,10 +145,10 @@ def test_next_rows_graph_replay_matches_eager():
     wt = torch.empty((B, hq), dtype=torch.float32, **cuda)
     outs = [torch.empty((B, hq, 128), dtype=torch.float32, **cuda) for _ in range(3)]
     ws_i = torch.empty(sdi.index_topk_workspace_bytes(dev.kv, hq, k_max), dtype=torch.uint8, **cuda)
-    ws_a = torch.zeros(max(1, sdi.attend_workspace_bytes(dev.kv, hq, 16 * m)), dtype=torch.uint8, **cuda)
+    ws_a = torch.empty(max(1, sdi.attend_workspace_bytes(dev.kv, hq, 16 * m)), dtype=torch.uint8, **cuda)
     ws_q = torch.empty(max(1, sdi.load_library().sparse_decode_quest_select_workspace(
         __import__("ctypes").byref(dev.kv.struct()), hq, m)), dtype=torch.uint8, **cuda)
-    ws_s = torch.zeros(max(1, sdi.attend_sampled_workspace_bytes(dev.kv, hq, kd_max, s_max)), dtype=torch.uint8,
+    ws_s = torch.empty(max(1, sdi.attend_sampled_workspace_bytes(dev.kv, hq, kd_max, s_max)), dtype=torch.uint8,
                        **cuda)
 
     def step():

@@ -368,7 +368,7 @@ def test_graph_replay_matches_eager():
     out = torch.empty((B, hq, 128), dtype=torch.float32, device="cuda")
     dn = torch.empty_like(out)
     ws_i = torch.empty(sdi.index_topk_workspace_bytes(dev.kv, hq, k_max), dtype=torch.uint8, device="cuda")
-    ws_a = torch.zeros(max(1, sdi.attend_workspace_bytes(dev.kv, hq, k_max)), dtype=torch.uint8, device="cuda")
+    ws_a = torch.empty(max(1, sdi.attend_workspace_bytes(dev.kv, hq, k_max)), dtype=torch.uint8, device="cuda")
     ws_d = torch.empty(sdi.dense_workspace_bytes(dev.kv, hq), dtype=torch.uint8, device="cuda")
 
     def step():
