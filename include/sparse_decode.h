@@ -58,7 +58,8 @@ enum {
     SDI_ERR_SHAPE = -2,      /* head_dim != 128, page_size != 16, heads not a multiple, sizes < 1 ... */
     SDI_ERR_K = -3,          /* k_max < 1 (pages_max < 1 for the page selection, s_max < 1 for draws) */
     SDI_ERR_WORKSPACE = -4,  /* workspace smaller than the *_workspace() size */
-    SDI_ERR_HIP = -5         /* a kernel launch failed */
+    SDI_ERR_HIP = -5,        /* a kernel launch failed */
+    SDI_ERR_TOO_LARGE = -6   /* more than the fixed scratch of sparse_decode_attend_noalloc holds */
 };
 
 /*
@@ -121,6 +122,22 @@ SDI_API int sparse_decode_attend(const sdi_kv *kv, const void *q, int32_t num_q_
                          void *ws, size_t ws_bytes, void *stream);
 
 SDI_API size_t sparse_decode_attend_workspace(const sdi_kv *kv, int32_t num_q_heads, int32_t k_max);
+
+/*
+ * sparse_decode_attend without a workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation).  Same arguments, checks and result as sparse_decode_attend, minus ws and
+ * ws_bytes; it allocates nothing.  Rows longer than 1024 entries are split into chunks
+ * whose partial results go to a fixed 32 MiB device array that the library holds on
+ * each GPU it runs on until the process ends (rows up to 1024 entries need none).  A
+ * call whose partials would not fit -- sparse_decode_attend_workspace() above 32 MiB,
+ * i.e. 520 * batch * num_q_heads * ceil(k_max / 256) bytes -- returns SDI_ERR_TOO_LARGE
+ * and launches nothing.  Every call on a GPU shares that array: calls that overlap on
+ * one GPU (on different streams) race.
+ */
+SDI_API int sparse_decode_attend_noalloc(const sdi_kv *kv, const void *q, int32_t num_q_heads, const int32_t *idx,
+                                         const int32_t *k_per_seq, int32_t k_max, float softmax_scale, float *out,
+                                         void *stream);
 
 /*
  * Dense decode (paper Fig. 1a dense mode: the whole cache is read every step).

@@ -22,10 +22,11 @@ PAGE_SIZE = 16
 DEFAULT_SCALE = 1.0 / math.sqrt(HEAD_DIM)
 
 SDI_OK, SDI_ERR_NULL, SDI_ERR_SHAPE, SDI_ERR_K, SDI_ERR_WORKSPACE, SDI_ERR_HIP = 0, -1, -2, -3, -4, -5
+SDI_ERR_TOO_LARGE = -6
 
 EXPORTS = (
     "sparse_decode_index_topk", "sparse_decode_index_topk_workspace",
-    "sparse_decode_attend", "sparse_decode_attend_workspace",
+    "sparse_decode_attend", "sparse_decode_attend_workspace", "sparse_decode_attend_noalloc",
     "dense_decode", "dense_decode_workspace", "sparse_decode_strerror",
     "sparse_decode_quest_summary_bytes", "sparse_decode_quest_summarize",
     "sparse_decode_quest_select", "sparse_decode_quest_select_workspace",
@@ -72,6 +73,8 @@ def load_library(path: str = LIB_PATH):
     lib.sparse_decode_attend.restype = ctypes.c_int
     lib.sparse_decode_attend_workspace.argtypes = [kvp, i32, i32]
     lib.sparse_decode_attend_workspace.restype = sz
+    lib.sparse_decode_attend_noalloc.argtypes = [kvp, p, i32, p, p, i32, f32, p, p]
+    lib.sparse_decode_attend_noalloc.restype = ctypes.c_int
     lib.dense_decode.argtypes = [kvp, p, i32, f32, p, p, sz, p]
     lib.dense_decode.restype = ctypes.c_int
     lib.dense_decode_workspace.argtypes = [kvp, i32]
@@ -263,6 +266,29 @@ def attend(kv: PagedKV, q, idx, k_per_seq=None, softmax_scale: float = DEFAULT_S
                                   _stream(stream))
     if rc != SDI_OK:
         raise SparseDecodeError(rc, "sparse_decode_attend")
+    return out
+
+
+def attend_noalloc(kv: PagedKV, q, idx, k_per_seq=None, softmax_scale: float = DEFAULT_SCALE, out=None,
+                   stream=None):
+    """attend() without a workspace (sparse_decode_attend_noalloc): split rows keep their
+    partials in the library's fixed 32 MiB per-GPU scratch.  With out given, nothing is
+    allocated; calls that overlap on one GPU race."""
+    import torch
+    hq = _check_q(kv, q)
+    B = kv.batch
+    _check(idx, "idx", torch.int32, 3, (B, hq, None))
+    _check_counts(kv, k_per_seq, "k_per_seq")
+    if out is None:
+        out = torch.empty((B, hq, HEAD_DIM), dtype=torch.float32, device=q.device)
+    _check(out, "out", torch.float32, 3, (B, hq, HEAD_DIM))
+    _on_device(q=q, idx=idx, k_per_seq=k_per_seq, out=out)
+    s = kv.struct()
+    rc = load_library().sparse_decode_attend_noalloc(ctypes.byref(s), _ptr(q), hq, _ptr(idx), _ptr(k_per_seq),
+                                                     int(idx.shape[2]), float(softmax_scale), _ptr(out),
+                                                     _stream(stream))
+    if rc != SDI_OK:
+        raise SparseDecodeError(rc, "sparse_decode_attend_noalloc")
     return out
 
 

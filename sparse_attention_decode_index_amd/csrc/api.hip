@@ -87,6 +87,21 @@ int sparse_decode_attend(const sdi_kv *kv, const void *q, int32_t num_q_heads, c
     return hip_status(sdi::launch_attend(a, (hipStream_t)stream));
 }
 
+int sparse_decode_attend_noalloc(const sdi_kv *kv, const void *q, int32_t num_q_heads, const int32_t *idx,
+                                 const int32_t *k_per_seq, int32_t k_max, float softmax_scale, float *out,
+                                 void *stream)
+{
+    int rc = check_kv(kv, true);
+    if (rc) return rc;
+    if (!q || !idx || !out) return SDI_ERR_NULL;
+    if ((rc = check_heads(kv, num_q_heads))) return rc;
+    if (k_max < 1) return SDI_ERR_K;
+    sdi::AttendArgs a{kv->k_cache, kv->v_cache, kv->page_table, kv->seq_lens, kv->batch, kv->num_kv_heads,
+                      kv->max_pages_per_seq, kv->n_max, q, num_q_heads, idx, k_per_seq, k_max, softmax_scale,
+                      out, nullptr};
+    return sdi::launch_attend_noalloc(a, (hipStream_t)stream);
+}
+
 int dense_decode(const sdi_kv *kv, const void *q, int32_t num_q_heads, float softmax_scale, float *out, void *ws,
                  size_t ws_bytes, void *stream)
 {
@@ -227,6 +242,7 @@ const char *sparse_decode_strerror(int code)
     case SDI_ERR_K: return "k_max (or pages_max, s_max) must be at least 1";
     case SDI_ERR_WORKSPACE: return "workspace smaller than the size the *_workspace() query returns";
     case SDI_ERR_HIP: return "a HIP kernel launch failed";
+    case SDI_ERR_TOO_LARGE: return "the call needs more than the fixed 32 MiB scratch of the allocation-free entry point";
     default: return "unknown sparse_decode status";
     }
 }

@@ -26,6 +26,9 @@
 // are not merged, as chunks past k'_b are in the one-list mode.
 #include "sdi_device.hpp"
 #include "sdi_launch.hpp"
+#include "../../include/sparse_decode.h"
+
+#include <mutex>
 
 namespace sdi {
 
@@ -328,6 +331,40 @@ static hipError_t launch_attend_mode(const AttendArgs &a, hipStream_t stream)
 hipError_t launch_attend(const AttendArgs &a, hipStream_t stream)
 {
     return a.sample ? launch_attend_mode<true>(a, stream) : launch_attend_mode<false>(a, stream);
+}
+
+// ---- allocation-free form ----------------------------------------------------------------
+// For callers that cannot allocate device memory (code under HIP graph capture, tight
+// serving loops): the chunk partials of rows longer than one workgroup go to one fixed
+// device array per GPU instead of a caller workspace.  Each call writes the partials it
+// merges before merge_kernel reads them, so nothing in the array has to start at zero;
+// calls that overlap on one GPU share the array and race.
+constexpr size_t kNoAllocBytes = (size_t)32 << 20;                      // 32 MiB per GPU
+static __device__ __align__(256) unsigned char scratch[kNoAllocBytes];
+
+constexpr int kMaxDevices = 64;
+static std::mutex scratch_mu;
+static void *scratch_ptr[kMaxDevices];                                   // its device address, per GPU
+
+int launch_attend_noalloc(AttendArgs a, hipStream_t stream)
+{
+    if (attend_workspace_bytes(a.batch, a.num_q_heads, a.k_max) > kNoAllocBytes) return SDI_ERR_TOO_LARGE;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return SDI_ERR_HIP;
+    void *base = nullptr;
+    {
+        // the array's address on this GPU, looked up on the first call there (host code
+        // must not pass the array's name itself: on the host that is only a stand-in)
+        std::lock_guard<std::mutex> lock(scratch_mu);
+        if (!scratch_ptr[dev]) {
+            void *p = nullptr;
+            if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return SDI_ERR_HIP;
+            scratch_ptr[dev] = p;
+        }
+        base = scratch_ptr[dev];
+    }
+    a.ws = base;
+    return launch_attend(a, stream) == hipSuccess ? SDI_OK : SDI_ERR_HIP;
 }
 
 }  // namespace sdi

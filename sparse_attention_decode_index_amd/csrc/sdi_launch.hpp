@@ -88,6 +88,9 @@ hipError_t launch_index_topk(const IndexArgs &a, hipStream_t stream);
 int attend_splits(int k_max);
 size_t attend_workspace_bytes(int batch, int num_q_heads, int k_max);
 hipError_t launch_attend(const AttendArgs &a, hipStream_t stream);
+// The allocation-free form of launch_attend: the partials of split rows go to a fixed
+// device array (a.ws is ignored).  Returns 0, SDI_ERR_TOO_LARGE or SDI_ERR_HIP.
+int launch_attend_noalloc(AttendArgs a, hipStream_t stream);
 hipError_t launch_sample(const SampleArgs &a, hipStream_t stream);
 
 hipError_t launch_merge(const float *part_ml, const float *part_acc, int splits, int per_chunk,

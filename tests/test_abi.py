@@ -43,7 +43,7 @@ def test_struct_layout_matches_header():
 
 
 def test_strerror_covers_every_code(lib):
-    for code in (0, -1, -2, -3, -4, -5):
+    for code in (0, -1, -2, -3, -4, -5, -6):
         s = sdi.strerror(code)
         assert s and "unknown" not in s
     assert "unknown" in sdi.strerror(42)
