@@ -54,9 +54,14 @@ constexpr int kGatherUnroll = 4;                              // candidates in f
 constexpr int kStageRow = kRowBytes + 16;                     // padded LDS row: conflict-free both ways
 constexpr int kStagePage = kPage * kStageRow;                 // 4352 B
 constexpr int kSubCap = kCandCap / 4;                         // ... as 4 lane lists (one per quad) of 48
-constexpr int kSubStride = kSubCap + 1;                       // padded: lists start in different banks
+constexpr int kSubStride = kSubCap + 1;                       // entries of a list, with its pad slot
+constexpr int kLists = kHeadBlock * 4;                        // lane lists of a wave (head, quad)
 constexpr int kSamplePagesPerWave = 16;                       // the first pages of each wave ...
 constexpr int kBlockSample = kScoreWaves * kSamplePagesPerWave * kPage;   // ... 1024 tokens per head
+constexpr int kSampStride = kBlockSample + 16;
+// Sample codes of head h start at h * kSampStride: the pad (16 codes, 8 banks) puts the
+// head rows of one write 8 banks apart, so the 32 head lanes of a page write (8 heads x 4
+// quads, 2 banks apart within a head) all land in different banks.
 constexpr int kSampleGroups = kSamplePagesPerWave / kScoreUnroll;
 static_assert(kSampleGroups % 2 == 0 && kSamplePagesPerWave <= kScorePagesPerWave, "sample = pairs of groups");
 
@@ -128,8 +133,8 @@ __global__ __launch_bounds__(kScoreWaves * 64, 2) void score_kernel(
 {
     __shared__ int32_t pt_lds[kSlots * kScoreWaves * kScorePagesPerWave];
     __shared__ __attribute__((aligned(16))) unsigned char stage_all[kScoreWaves * kScoreUnroll * kStagePage];
-    __shared__ uint32_t ck_all[kScoreWaves * kHeadBlock * 4 * kSubStride];
-    __shared__ __attribute__((aligned(16))) uint16_t samp[kHeadBlock][kBlockSample];   // top 16 key bits
+    __shared__ uint32_t ck_all[kScoreWaves * kLists * kSubStride];
+    __shared__ __attribute__((aligned(16))) uint16_t samp[kHeadBlock * kSampStride];   // top 16 key bits
     __shared__ uint32_t lo_lds[kHeadBlock];
     __shared__ __attribute__((aligned(16))) uint16_t q_lds[kHeadBlock * kHeadDim];
     const int b = blockIdx.z;
@@ -146,8 +151,10 @@ __global__ __launch_bounds__(kScoreWaves * 64, 2) void score_kernel(
     const int col = lane & 15, quad = lane >> 4;
     const bool head_lane = col < heads_here;                  // lanes of column col carry head col
     unsigned char *stage = stage_all + wave * kScoreUnroll * kStagePage;
-    uint32_t *ck = ck_all + wave * kHeadBlock * 4 * kSubStride;
-    const int my_list = (min(col, kHeadBlock - 1) * 4 + quad) * kSubStride;   // this lane's list (head col, quad)
+    // Lane lists are interleaved entry by entry (entry e of list L at e * kLists + L), so
+    // the 32 head lanes of an append, whatever their counts, write 32 different banks.
+    uint32_t *ck = ck_all + wave * kLists * kSubStride;
+    const int my_list = min(col, kHeadBlock - 1) * 4 + quad;   // this lane's list (head col, quad)
 
     const int pages_seq = (n + kPage - 1) / kPage;
     const int p_base = tok0 / kPage;                          // first page of this workgroup
@@ -246,7 +253,7 @@ __global__ __launch_bounds__(kScoreWaves * 64, 2) void score_kernel(
         for (int i = 0; i < 4; ++i) {
             const bool take = (t0 + i < n) & (__uint_as_float(sc[i]) >= lo_f);
             const uint32_t at = (take & (cnt < (uint32_t)kSubCap)) ? cnt : (uint32_t)kSubCap;
-            ck[my_list + at] = sc[i];
+            ck[at * kLists + my_list] = sc[i];
             taken[(4 * po + i) >> 5] |= (take ? 1u : 0u) << ((4 * po + i) & 31);
             cnt += take ? 1u : 0u;
         }
@@ -290,7 +297,7 @@ __global__ __launch_bounds__(kScoreWaves * 64, 2) void score_kernel(
                 skey[su][i] = sc[i];
                 const int t = pp * kPage + 4 * quad + i;
                 if (head_lane)
-                    samp[col][(wave * kSamplePagesPerWave + su) * kPage + 4 * quad + i] =
+                    samp[col * kSampStride + (wave * kSamplePagesPerWave + su) * kPage + 4 * quad + i] =
                         (pp < p_end && t < n) ? (uint16_t)(score_key(__uint_as_float(sc[i])) >> 16) : (uint16_t)0;
             }
         }
@@ -331,7 +338,7 @@ __global__ __launch_bounds__(kScoreWaves * 64, 2) void score_kernel(
                 uint32_t c[per_lane];
 #pragma unroll
                 for (int v = 0; v < per_lane / 8; ++v) {
-                    const u32x4 w4 = *(const u32x4 *)&samp[hh][lane * per_lane + 8 * v];
+                    const u32x4 w4 = *(const u32x4 *)&samp[hh * kSampStride + lane * per_lane + 8 * v];
                     c[8 * v + 0] = w4.x & 0xFFFFu; c[8 * v + 1] = w4.x >> 16;
                     c[8 * v + 2] = w4.y & 0xFFFFu; c[8 * v + 3] = w4.y >> 16;
                     c[8 * v + 4] = w4.z & 0xFFFFu; c[8 * v + 5] = w4.z >> 16;
@@ -370,9 +377,10 @@ __global__ __launch_bounds__(kScoreWaves * 64, 2) void score_kernel(
         // 128-byte lines: a partial line costs HBM a read-modify-write, and these
         // writes share the memory with the key stream.
         uint32_t *out_key = (uint32_t *)stage;                                 // [head][kCandCap]
-        uint32_t *out_tail = (uint32_t *)(&samp[0][0] + wave * (kHeadBlock * kBlockSample / kScoreWaves));
+        uint32_t *out_tail = (uint32_t *)(samp + wave * (kHeadBlock * kSampStride / kScoreWaves));
         static_assert(kHeadBlock * kCandCap * 4 <= kScoreUnroll * kStagePage, "keys fit the stage tile");
-        static_assert(kHeadBlock * kRecTailWords * 4 <= kHeadBlock * kBlockSample * 2 / kScoreWaves, "tails fit");
+        static_assert(kHeadBlock * kRecTailWords * 4 <= kHeadBlock * kSampStride * 2 / kScoreWaves, "tails fit");
+        static_assert(kHeadBlock * kSampStride * 2 / kScoreWaves % 16 == 0, "tails 16-byte aligned");
         wave_lds_sync();
         const int slot = p_begin / kScorePagesPerWave;
         uint32_t oc[4], om[4][4], total = 0;
@@ -415,7 +423,7 @@ __global__ __launch_bounds__(kScoreWaves * 64, 2) void score_kernel(
 #pragma unroll
                     for (int q2 = 0; q2 < 4; ++q2)
                         if (q2 != quad) f += (uint32_t)__popc(om[q2][w] & (q2 < quad ? m_lo : m_hi));
-                    const uint32_t key = score_key(__uint_as_float(ck[my_list + e]));
+                    const uint32_t key = score_key(__uint_as_float(ck[e * kLists + my_list]));
                     kmax = max(kmax, key);
                     out_key[col * kCandCap + f] = key;
                     tail_pos[f] = (uint16_t)(pg * kPage + 4 * quad + (j & 3));

@@ -58,7 +58,7 @@ def test_workspace_sizes(lib):
     assert n1 == 2 * 8 * (256 * 4 + 1 * 1280)
     assert lib.sparse_decode_attend_workspace(ctypes.byref(k), 8, 1024) == 0         # one chunk: no partials
     assert lib.sparse_decode_attend_workspace(ctypes.byref(k), 8, 1025) == 2 * 8 * 5 * 130 * 4   # 256-entry chunks
-    assert lib.dense_decode_workspace(ctypes.byref(k), 8) == 2 * 8 * 1 * 130 * 4      # one 1024-token chunk
+    assert lib.dense_decode_workspace(ctypes.byref(k), 8) == 2 * 8 * 1 * 130 * 4      # one 4096-token chunk
     assert lib.sparse_decode_attend_workspace(None, 8, 5) == 0
 
 
