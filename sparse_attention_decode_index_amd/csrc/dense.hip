@@ -1,14 +1,14 @@
 // Dense decode over the whole paged cache (gfx950): the dense mode of the
 // context-sparsity paper's Fig. 1a, which reads every cached row each step.
 //
-// Every K/V row of a (b, kv head) serves all G query heads of its group, so
-// q K^T is a real [G x 128] x [128 x 16] contraction per page and runs on the
-// bf16 MFMA (16x16x32; head rows padded to 16).  The p V product keeps fp32
-// weights and runs on the vector ALU: each 16-lane group owns 4 of the page's 16
-// rows and 8 of the 128 dims, and reads the weights of its rows from LDS.
-// Softmax uses FlashAttention's running (max, sum, accumulator) update (survey
-// page, section 5.1).  A workgroup of 4 waves covers 256 pages (4096 tokens), each
-// wave 64 pages with the next page's K and V in flight; the 4 wave states are
+// Every K/V row of a (b, kv head) serves all G query heads of its group, so both
+// products are real contractions over the group and run on the bf16 MFMA
+// (16x16x32, head rows padded to 16): q K^T ([G x 128] x [128 x 32 tokens]) and
+// P V ([G x 32 tokens] x [32 x 128]), the weights P rounded to bf16.  V's rows are
+// transposed into the MFMA operand through LDS.  Softmax uses FlashAttention's
+// running (max, sum, accumulator) update (survey page, section 5.1).  A workgroup of
+// 4 waves covers 256 pages (4096 tokens), each wave 64 pages, two at a time with the
+// next two pages' K and V in flight; the 4 wave states are
 // merged in LDS into one partial per workgroup, and the partials of a sequence are
 // combined by the same log-sum-exp merge as the sparse path.
 #include "sdi_device.hpp"
@@ -26,15 +26,37 @@ constexpr int kDenseTokensPerSplit = kDenseWaves * kDensePagesPerWave * kPage;  
 static_assert(kDensePagesPerWave <= 64, "one page-table entry per lane");
 constexpr float kDenseLog2e = 1.4426950408889634f;
 
-__device__ __forceinline__ void wave_sync_lds()
+
+// LDS tiles of a wave: the V rows of two pages (32 tokens x 128 dims, bf16, rows of
+// 132 values: 264 B, 8-byte aligned) and the bf16 weights P[head][token] of those 32
+// tokens (rows of 40 values).  The row strides put the transposed operand reads in
+// different banks: V row r + 8 starts 16 banks after row r, so the four 16-lane groups
+// of a read (tokens 8 quad + e) cover disjoint banks; P rows of the 16 heads start 20
+// banks apart.
+constexpr int kVStride = kHeadDim + 4;
+constexpr int kPStride = 2 * kPage + 8;
+constexpr int kVTile = 2 * kPage * kVStride;                  // bf16 values per wave
+constexpr int kPTile = 16 * kPStride;
+
+// bf16 bits of a finite fp32 value, round to nearest even
+__device__ __forceinline__ uint32_t bf16_bits_rne(float x)
 {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const uint32_t u = __float_as_uint(x);
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
 // grid (splits, num_kv_heads * head_blocks, batch); 256 threads.
-// NH = head rows carried per wave (>= heads in this head block, <= 16).
+// NH = head rows kept for the merge (>= heads in this head block, <= 16).
+//
+// Per wave and per pair of pages (32 tokens): S = q K^T on 8 MFMAs (A = q, 16 head
+// rows; B = K, one token per column) gives lane (col, quad) the scores of token col
+// for heads 4 quad + i.  The running max, the rescale factor and the weights follow
+// the online softmax per head; the weights are rounded to bf16, and the row sums
+// accumulate those rounded weights, so numerator and denominator use the same values.
+// The weights go to LDS as P[head][token] and the V rows as [token][dim]; then
+// O += P V runs on 8 more MFMAs (A = P: head col, tokens 8 quad .. +7; B = V: tokens
+// 8 quad .. +7, dim col + 16 j), and lane (col, quad) ends with O[heads 4 quad + i]
+// [dims col + 16 j].  The next pair's K and V are in flight meanwhile.
 template <int NH>
 __global__ __launch_bounds__(kDenseWaves * 64) void dense_kernel(
     const uint16_t *__restrict__ kc, const uint16_t *__restrict__ vc, const int32_t *__restrict__ page_table,
@@ -42,9 +64,9 @@ __global__ __launch_bounds__(kDenseWaves * 64) void dense_kernel(
     int group, int head_blocks, int max_pages, float scale_log2, int splits, float *__restrict__ part_ml,
     float *__restrict__ part_acc)
 {
-    __shared__ float p_lds[kDenseWaves][kPage][16];           // [token][head]
-    __shared__ float a_lds[kDenseWaves][16];                  // rescale factor per head
-    __shared__ float w_acc[kDenseWaves][NH][kHeadDim];        // per-wave accumulators for the merge
+    static_assert(NH * kHeadDim * 4 <= kVTile * 2, "the merge rows fit a wave's V tile");
+    __shared__ __attribute__((aligned(16))) uint16_t v_lds[kDenseWaves][kVTile];
+    __shared__ __attribute__((aligned(16))) uint16_t p_lds[kDenseWaves][kPTile];
     __shared__ float w_ml[kDenseWaves][NH][2];
     const int b = blockIdx.z;
     const int g = blockIdx.y / head_blocks, hb = blockIdx.y - g * head_blocks;
@@ -59,17 +81,17 @@ __global__ __launch_bounds__(kDenseWaves * 64) void dense_kernel(
     const int p_end = min(p_begin + kDensePagesPerWave, pages_seq);
     const int heads_here = min(16, group - hb * 16);
     const int h0 = g * group + hb * 16;
+    uint16_t *vt = v_lds[wave];
+    uint16_t *pt_w = p_lds[wave];
 
     float mrow[4], lpart[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) { mrow[i] = -INFINITY; lpart[i] = 0.f; }
-    float acc[NH][8];
+    f32x4 o[8];
 #pragma unroll
-    for (int hh = 0; hh < NH; ++hh)
-#pragma unroll
-        for (int d = 0; d < 8; ++d) acc[hh][d] = 0.f;
+    for (int j = 0; j < 8; ++j) o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    if (p_begin < p_end) {                                    // wave-uniform; no barriers inside
+    if (p_begin < p_end) {                                    // wave-uniform; no workgroup barriers inside
         bf16x8 qa[4];
         {
             const bool live = col < heads_here;
@@ -81,108 +103,112 @@ __global__ __launch_bounds__(kDenseWaves * 64) void dense_kernel(
         }
         const int32_t *pt = page_table + (int64_t)b * max_pages;
         const int pt_lane = (p_begin + lane < p_end) ? pt[p_begin + lane] : 0;   // the wave's entries, one per lane
-        const int koff = col * kHeadDim + quad * 8;           // MFMA B operand: token col, dims 32 s + 8 quad
-        const int voff = quad * kHeadDim + col * 8;           // rows quad + 4 rr, dims 8 col .. +7 (1 KiB rows)
+        const int koff = col * kHeadDim + quad * 8;           // K operand: token col, dims 32 s + 8 quad
+        const int voff = quad * kHeadDim + col * 8;           // V rows quad + 4 rr, dims 8 col .. +7
 
-        bf16x8 kb[4];
-        u32x4 vw[4];
-        {
-            const int64_t blk = ((int64_t)__builtin_amdgcn_readlane(pt_lane, 0) * num_kv_heads + g) * (kPage * kHeadDim);
+        // K and V of pages p, p + 1 (a page past the wave's range re-reads its last page;
+        // its tokens are masked below)
+        auto load_pair = [&](int p, bf16x8 (&kb)[2][4], u32x4 (&vw)[2][4]) {
 #pragma unroll
-            for (int s = 0; s < 4; ++s) kb[s] = *(const bf16x8 *)(kc + blk + koff + 32 * s);
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr)
-                vw[rr] = __builtin_nontemporal_load((const u32x4 *)(vc + blk + voff + rr * 4 * kHeadDim));
-        }
-
-        for (int p = p_begin; p < p_end; ++p) {
-            // the next page's K and V are in flight while this one is processed
-            bf16x8 kb_n[4];
-            u32x4 vw_n[4];
-            {
-                const int pn = min(p + 1, p_end - 1);
+            for (int pp = 0; pp < 2; ++pp) {
+                const int pg = min(p + pp, p_end - 1);
                 const int64_t blk =
-                    ((int64_t)__builtin_amdgcn_readlane(pt_lane, pn - p_begin) * num_kv_heads + g) * (kPage * kHeadDim);
+                    ((int64_t)__builtin_amdgcn_readlane(pt_lane, pg - p_begin) * num_kv_heads + g) * (kPage * kHeadDim);
 #pragma unroll
-                for (int s = 0; s < 4; ++s) kb_n[s] = *(const bf16x8 *)(kc + blk + koff + 32 * s);
+                for (int s = 0; s < 4; ++s) kb[pp][s] = *(const bf16x8 *)(kc + blk + koff + 32 * s);
 #pragma unroll
                 for (int rr = 0; rr < 4; ++rr)
-                    vw_n[rr] = __builtin_nontemporal_load((const u32x4 *)(vc + blk + voff + rr * 4 * kHeadDim));
+                    vw[pp][rr] = __builtin_nontemporal_load((const u32x4 *)(vc + blk + voff + rr * 4 * kHeadDim));
             }
+        };
+        bf16x8 kb[2][4];
+        u32x4 vw[2][4];
+        load_pair(p_begin, kb, vw);
 
-            f32x4 s4 = {0.f, 0.f, 0.f, 0.f};
+        for (int p = p_begin; p < p_end; p += 2) {
+            bf16x8 kb_n[2][4];
+            u32x4 vw_n[2][4];
+            load_pair(min(p + 2, p_end - 1), kb_n, vw_n);     // the next pair, in flight
+
+            f32x4 s4[2];
 #pragma unroll
-            for (int s = 0; s < 4; ++s) s4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[s], kb[s], s4, 0, 0, 0);
-            const bool tv = p * kPage + col < n;                  // token `col` of this page exists
-            float pn_[4], alpha[4];
+            for (int pp = 0; pp < 2; ++pp) {
+                s4[pp] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s = 0; s < 4; ++s) s4[pp] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[s], kb[pp][s], s4[pp], 0, 0, 0);
+            }
+            float alpha[4], w[2][4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float x = tv ? s4[i] * scale_log2 : -INFINITY;
-                const float mx = row16_max(x);                     // finite: the page's first token exists
+                float x[2];
+#pragma unroll
+                for (int pp = 0; pp < 2; ++pp) {
+                    const bool tv = (p + pp < p_end) && (p + pp) * kPage + col < n;   // token col of page p + pp
+                    x[pp] = tv ? s4[pp][i] * scale_log2 : -INFINITY;
+                }
+                const float mx = fmaxf(row16_max(x[0]), row16_max(x[1]));   // finite: page p's first token exists
                 const float mn = fmaxf(mrow[i], mx);
                 alpha[i] = fast_exp2(mrow[i] - mn);
-                pn_[i] = fast_exp2(x - mn);
-                mrow[i] = mn;
-                lpart[i] = lpart[i] * alpha[i] + pn_[i];
-            }
+                float ls = 0.f;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) p_lds[wave][col][quad * 4 + i] = pn_[i];
-            if (col == 0) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) a_lds[wave][quad * 4 + i] = alpha[i];
-            }
-            wave_sync_lds();
-#pragma unroll
-            for (int hh = 0; hh < NH; ++hh) {
-                const float a = a_lds[wave][hh];
-#pragma unroll
-                for (int d = 0; d < 8; ++d) acc[hh][d] *= a;
-            }
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-                float vf[8];
-                unpack8(vw[rr], vf);
-                const float *prow = p_lds[wave][quad + 4 * rr];
-#pragma unroll
-                for (int hh = 0; hh < NH; ++hh) {
-                    const float pp = prow[hh];
-#pragma unroll
-                    for (int d = 0; d < 8; ++d) acc[hh][d] = fmaf(pp, vf[d], acc[hh][d]);
+                for (int pp = 0; pp < 2; ++pp) {
+                    const uint32_t wb = bf16_bits_rne(fast_exp2(x[pp] - mn));
+                    w[pp][i] = __uint_as_float(wb << 16);
+                    ls += w[pp][i];
+                    pt_w[(4 * quad + i) * kPStride + kPage * pp + col] = (uint16_t)wb;
                 }
+                mrow[i] = mn;
+                lpart[i] = lpart[i] * alpha[i] + ls;
             }
-            wave_sync_lds();
+            // V rows of the pair to LDS: row 16 pp + quad + 4 rr, dims 8 col .. +7 (two 8-byte writes)
 #pragma unroll
-            for (int s = 0; s < 4; ++s) kb[s] = kb_n[s];
+            for (int pp = 0; pp < 2; ++pp)
 #pragma unroll
-            for (int rr = 0; rr < 4; ++rr) vw[rr] = vw_n[rr];
+                for (int rr = 0; rr < 4; ++rr) {
+                    uint2 *dst = (uint2 *)(vt + (kPage * pp + quad + 4 * rr) * kVStride + 8 * col);
+                    dst[0] = uint2{vw[pp][rr].x, vw[pp][rr].y};
+                    dst[1] = uint2{vw[pp][rr].z, vw[pp][rr].w};
+                }
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) o[j][i] *= alpha[i];
+            wave_lds_sync();
+            const bf16x8 pa = *(const bf16x8 *)(pt_w + col * kPStride + 8 * quad);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const uint16_t *src = vt + 8 * quad * kVStride + col + 16 * j;
+                u32x4 vb;
+                vb.x = (uint32_t)src[0 * kVStride] | ((uint32_t)src[1 * kVStride] << 16);
+                vb.y = (uint32_t)src[2 * kVStride] | ((uint32_t)src[3 * kVStride] << 16);
+                vb.z = (uint32_t)src[4 * kVStride] | ((uint32_t)src[5 * kVStride] << 16);
+                vb.w = (uint32_t)src[6 * kVStride] | ((uint32_t)src[7 * kVStride] << 16);
+                o[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, __builtin_bit_cast(bf16x8, vb), o[j], 0, 0, 0);
+            }
+            wave_lds_sync();                                  // tiles free for the next pair
+#pragma unroll
+            for (int pp = 0; pp < 2; ++pp) {
+#pragma unroll
+                for (int s = 0; s < 4; ++s) kb[pp][s] = kb_n[pp][s];
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) vw[pp][rr] = vw_n[pp][rr];
+            }
         }
     }
 
-    // This wave's state: per head row sums (D layout) and accumulators summed over the
-    // 4 lane groups (lanes xor 16 / 32 hold the same dims of different rows).
+    // This wave's state: per head row sums, and O straight from the MFMA layout into the
+    // wave's own V tile, reused as its [head][dim] merge rows.
+    float *w_acc = (float *)vt;
     float lrow[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) lrow[i] = row16_sum(lpart[i]);
 #pragma unroll
-    for (int hh = 0; hh < NH; ++hh)
+    for (int i = 0; i < 4; ++i) {
+        const int hm = quad * 4 + i;
+        if (hm < NH) {
 #pragma unroll
-        for (int d = 0; d < 8; ++d) {
-            float a = acc[hh][d];
-            a += __shfl_xor(a, 16, 64);
-            a += __shfl_xor(a, 32, 64);
-            acc[hh][d] = a;
-        }
-    if (quad == 0) {
-#pragma unroll
-        for (int hh = 0; hh < NH; ++hh)
-#pragma unroll
-            for (int d = 0; d < 8; ++d) w_acc[wave][hh][col * 8 + d] = acc[hh][d];
-    }
-    if (col == 0) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int hm = quad * 4 + i;
-            if (hm < NH) { w_ml[wave][hm][0] = mrow[i]; w_ml[wave][hm][1] = lrow[i]; }
+            for (int j = 0; j < 8; ++j) w_acc[hm * kHeadDim + col + 16 * j] = o[j][i];
+            if (col == 0) { w_ml[wave][hm][0] = mrow[i]; w_ml[wave][hm][1] = lrow[i]; }
         }
     }
     __syncthreads();
@@ -199,7 +225,7 @@ __global__ __launch_bounds__(kDenseWaves * 64) void dense_kernel(
         for (int w = 0; w < kDenseWaves; ++w) {
             const float f = (M == -INFINITY) ? 0.f : fast_exp2(w_ml[w][hh][0] - M);
             L += f * w_ml[w][hh][1];
-            A += f * w_acc[w][hh][d];
+            A += f * ((const float *)v_lds[w])[hh * kHeadDim + d];
         }
         const int64_t ps = (bh0 + hh) * splits + split;
         part_acc[ps * kHeadDim + d] = A;
