@@ -96,7 +96,12 @@ typedef struct sdi_kv {
  *              tokens: the k' largest scores s_j = q . K_j (fp32 accumulation of
  *              bf16 products), ties going to the lower index.
  *   idx_out    int32 [batch][num_q_heads][k_max]: the k' indices ascending, then -1.
- *   ws         device workspace of at least sparse_decode_index_topk_workspace() bytes.
+ *   ws         device workspace of at least sparse_decode_index_topk_workspace() bytes:
+ *              per (b, h) a 32-bit key row of roundup(n_max, 128) entries (touched only
+ *              by the exact re-scoring fallback and, for k a large share of N, by the
+ *              all-keys mode) and a 1280-byte candidate record per 512 cached tokens --
+ *              about 2.15 GB for 32 x 64 rows of up to 161 566 tokens.  Any contents on
+ *              entry.
  * Reads k_cache only (v_cache may be NULL).
  */
 SDI_API int sparse_decode_index_topk(const sdi_kv *kv, const void *q, int32_t num_q_heads,
