@@ -669,19 +669,26 @@ __global__ __launch_bounds__(kThreads) void select_kernel(SelectArgs a)
     const uint32_t mask0 = (1u << w0) - 1u;
     uint32_t eligible = 0;                                    // keys >= lo this thread gathered
     for (uint32_t v0 = 0; v0 < total; v0 += kThreads * kGatherUnroll) {
-        uint32_t key[kGatherUnroll];
-        uint16_t ps[kGatherUnroll];
+        // every slot walk first, then every load, then their uses: a walk between two
+        // loads would reuse registers that a load in flight still has to write, and the
+        // load would be waited for before the next one goes out.  Positions past the
+        // list re-read the last entry (in place, unused).
+        const uint32_t *rec[kGatherUnroll];
+        uint32_t jj[kGatherUnroll];
 #pragma unroll
         for (int u = 0; u < kGatherUnroll; ++u) {
-            const uint32_t v = v0 + u * kThreads + threadIdx.x;
-            if (v < total) {
-                const int i = slot_of_position(first, blk, v);
-                const uint32_t *rec = rec_row + (int64_t)i * kRecWords;
-                const uint32_t j = v - first[i];
-                key[u] = rec[j];
-                ps[u] = ((const uint16_t *)(rec + kCandCap + 4))[j];
-            }
+            const uint32_t v = min(v0 + u * kThreads + threadIdx.x, total - 1u);
+            const int i = slot_of_position(first, blk, v);
+            rec[u] = rec_row + (int64_t)i * kRecWords;
+            jj[u] = v - first[i];
         }
+        uint32_t key[kGatherUnroll], ps[kGatherUnroll];
+#pragma unroll
+        for (int u = 0; u < kGatherUnroll; ++u) {
+            key[u] = rec[u][jj[u]];
+            ps[u] = ((const uint16_t *)(rec[u] + kCandCap + 4))[jj[u]];
+        }
+        asm volatile("" ::: "memory");                        // the loads stay above their uses
 #pragma unroll
         for (int u = 0; u < kGatherUnroll; ++u) {
             const uint32_t v = v0 + u * kThreads + threadIdx.x;
