@@ -122,7 +122,8 @@ def test_group_sizes(hq, hkv):
     ([2500, 1000, 3333], [2500, 7, 999], 2600),         # k = N, ragged k
     ([4096, 2049], [4000, 2049], 4096),                 # k close to N
     ([9000], [8500], 8500),                              # k beyond the attend chunk count
-], ids=["k1", "k-ge-N", "ragged-k", "k-near-N", "big-k"])
+    ([3000, 5, 700, 40], [0, 5, 0, 3], 64),              # k = 0 rows: all -1, attend gives 0
+], ids=["k1", "k-ge-N", "ragged-k", "k-near-N", "big-k", "k0"])
 def test_k_edges(lens, kvec, k_max):
     rng = np.random.default_rng(len(lens) * 7 + k_max)
     case = random_case(rng, batch=len(lens), hq=8, hkv=2, lens=lens, layout="fragmented")
