@@ -137,8 +137,10 @@ SDI_API size_t sparse_decode_attend_workspace(const sdi_kv *kv, int32_t num_q_he
  * each GPU it runs on until the process ends (rows up to 1024 entries need none).  A
  * call whose partials would not fit -- sparse_decode_attend_workspace() above 32 MiB,
  * i.e. 520 * batch * num_q_heads * ceil(k_max / 256) bytes -- returns SDI_ERR_TOO_LARGE
- * and launches nothing.  Every call on a GPU shares that array: calls that overlap on
- * one GPU (on different streams) race.
+ * and launches nothing.  The GPU is the stream's (the current device for the null
+ * stream); the array's address there is looked up on the first call on that GPU.
+ * Every call on a GPU shares that array: calls that overlap on one GPU (on different
+ * streams) race.
  */
 SDI_API int sparse_decode_attend_noalloc(const sdi_kv *kv, const void *q, int32_t num_q_heads, const int32_t *idx,
                                          const int32_t *k_per_seq, int32_t k_max, float softmax_scale, float *out,

@@ -349,16 +349,29 @@ static void *scratch_ptr[kMaxDevices];                                   // its 
 int launch_attend_noalloc(AttendArgs a, hipStream_t stream)
 {
     if (attend_workspace_bytes(a.batch, a.num_q_heads, a.k_max) > kNoAllocBytes) return SDI_ERR_TOO_LARGE;
+    // the GPU the call runs on: the stream's (the current device for the null stream)
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return SDI_ERR_HIP;
+    if (stream) {
+        hipDevice_t d = 0;
+        if (hipStreamGetDevice(stream, &d) != hipSuccess) return SDI_ERR_HIP;
+        dev = (int)d;
+    } else if (hipGetDevice(&dev) != hipSuccess) {
+        return SDI_ERR_HIP;
+    }
+    if (dev < 0 || dev >= kMaxDevices) return SDI_ERR_HIP;
     void *base = nullptr;
     {
-        // the array's address on this GPU, looked up on the first call there (host code
-        // must not pass the array's name itself: on the host that is only a stand-in)
+        // the array's address on that GPU, looked up once with that GPU current (host
+        // code must not pass the array's name itself: on the host it is only a stand-in)
         std::lock_guard<std::mutex> lock(scratch_mu);
         if (!scratch_ptr[dev]) {
+            int cur = 0;
+            if (hipGetDevice(&cur) != hipSuccess) return SDI_ERR_HIP;
+            if (cur != dev && hipSetDevice(dev) != hipSuccess) return SDI_ERR_HIP;
             void *p = nullptr;
-            if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return SDI_ERR_HIP;
+            const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (cur != dev) (void)hipSetDevice(cur);
+            if (e != hipSuccess || !p) return SDI_ERR_HIP;
             scratch_ptr[dev] = p;
         }
         base = scratch_ptr[dev];
